@@ -1,0 +1,308 @@
+"""Python binding of libsage, the MI355X decode library for SAGE's 2.25-bit spherical VQ weights.
+
+"SAGE: Pushing 2-Bit Vector-Quantized LLMs toward Real-World Usability" defines the stored fields
+(§3.1: sign bits, codeword index, radius code, per-128-weight fp16 grid; §3.2: the ESG permutation)
+and the fused decode-and-multiply this library implements on gfx950.
+
+This module only marshals arguments: every step of the computation runs in the HIP kernels behind
+the C ABI in include/sage.h. PyTorch is used for device memory and streams. There is no CPU
+fallback: if libsage.so has not been built, importing the kernels' entry points raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsage.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "sage.h")
+
+SAGE_OK = 0
+
+
+class SageError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: status {status} ({status_string(status)})")
+
+
+class SageMatrix(ctypes.Structure):
+    """Mirror of sage_matrix_t."""
+
+    _fields_ = [
+        ("d_out", ctypes.c_int32), ("d_in", ctypes.c_int32),
+        ("log2K", ctypes.c_int32), ("V", ctypes.c_int32),
+        ("packed", ctypes.c_void_p), ("codebook", ctypes.c_void_p), ("pi", ctypes.c_void_p),
+    ]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+_PSZ = ctypes.POINTER(ctypes.c_size_t)
+_PM = ctypes.POINTER(SageMatrix)
+_PP = ctypes.POINTER(ctypes.c_void_p)
+_PI64 = ctypes.POINTER(ctypes.c_int64)
+
+_SIGNATURES = {
+    "sage_status_string": (ctypes.c_char_p, [_I]),
+    "sage_version": (_I, []),
+    "sage_format_version": (_I, []),
+    "sage_packed_bytes": (_I, [_I, _I, _I, _I, _PSZ]),
+    "sage_pack": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
+    "sage_unpack": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
+    "sage_dequant": (_I, [_PM, _P, _P]),
+    "sage_gemv_workspace_bytes": (_I, [_PM, _PSZ]),
+    "sage_gemv": (_I, [_PM, _P, _P, _P, _SZ, _P]),
+    "sage_gemv_multi_workspace_bytes": (_I, [_PM, _I, _PSZ]),
+    "sage_gemv_multi": (_I, [_PM, _PP, _PP, _I, _P, _SZ, _P]),
+    "sage_gemm_small_workspace_bytes": (_I, [_PM, _I, _PSZ]),
+    "sage_gemm_small": (_I, [_PM, _P, _I, _I, _P, _I, _P, _SZ, _P]),
+    "sage_moe_gemv_workspace_bytes": (_I, [_PM, _I, _I, _PSZ]),
+    "sage_moe_gemv": (_I, [_PM, _I, _PM, _I, _P, _I, _PP, _PI64, _PP, _PI64, _P, _SZ, _P]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libsage.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m bit_vector_quantized_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def header_functions() -> List[str]:
+    """Names of the functions declared in include/sage.h."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(sage_\w+)\s*\(", text, flags=re.M)))
+
+
+def status_string(status: int) -> str:
+    try:
+        return lib().sage_status_string(status).decode()
+    except Exception:  # pragma: no cover
+        return "?"
+
+
+def _check(fn: str, st: int) -> None:
+    if st != SAGE_OK:
+        raise SageError(fn, st)
+
+
+# ------------------------------------------------------------------------------------------------
+# torch glue
+# ------------------------------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libsage arguments must be device tensors")
+
+
+@dataclass
+class Packed:
+    """A packed matrix resident on the device (owns its buffers)."""
+
+    d_out: int
+    d_in: int
+    log2K: int
+    V: int
+    packed: "object"      # torch.uint8 [bytes]
+    codebook: "object"    # torch.float16 [K, 8]
+    pi: "object"          # torch.int32 [d_in] or None
+
+    def desc(self) -> SageMatrix:
+        return SageMatrix(self.d_out, self.d_in, self.log2K, self.V, _ptr(self.packed),
+                          _ptr(self.codebook), _ptr(self.pi))
+
+    @property
+    def K(self) -> int:
+        return 1 << self.log2K
+
+
+def packed_bytes(d_out: int, d_in: int, log2K: int, V: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("sage_packed_bytes", lib().sage_packed_bytes(d_out, d_in, log2K, V, ctypes.byref(n)))
+    return n.value
+
+
+def pack(signs, idx, rcode, mu, delta, codebook, pi, log2K: int, V: int, stream=None) -> Packed:
+    """Pack device field tensors (uint8 [d_out, d_in/8] x3, fp16 [d_out, d_in/128] x2) and keep
+    the codebook (fp16 [K, 8]) and permutation (int32 [d_in] or None) alongside."""
+    torch = _torch()
+    _require_cuda(signs, idx, rcode, mu, delta, codebook, pi)
+    d_out, m = signs.shape
+    d_in = m * 8
+    buf = torch.empty(packed_bytes(d_out, d_in, log2K, V), dtype=torch.uint8, device=signs.device)
+    _check("sage_pack", lib().sage_pack(_ptr(signs), _ptr(idx), _ptr(rcode), _ptr(mu), _ptr(delta),
+                                        d_out, d_in, log2K, V, _ptr(buf), _stream(stream)))
+    return Packed(d_out, d_in, log2K, V, buf, codebook, pi)
+
+
+def unpack(p: Packed, stream=None):
+    torch = _torch()
+    dev = p.packed.device
+    m, ng = p.d_in // 8, p.d_in // 128
+    signs = torch.empty((p.d_out, m), dtype=torch.uint8, device=dev)
+    idx = torch.empty_like(signs)
+    rcode = torch.empty_like(signs)
+    mu = torch.empty((p.d_out, ng), dtype=torch.float16, device=dev)
+    delta = torch.empty_like(mu)
+    _check("sage_unpack", lib().sage_unpack(_ptr(p.packed), p.d_out, p.d_in, p.log2K, p.V,
+                                            _ptr(signs), _ptr(idx), _ptr(rcode), _ptr(mu),
+                                            _ptr(delta), _stream(stream)))
+    return signs, idx, rcode, mu, delta
+
+
+def dequant(p: Packed, out=None, stream=None):
+    torch = _torch()
+    w = torch.empty((p.d_out, p.d_in), dtype=torch.float16, device=p.packed.device) \
+        if out is None else out
+    d = p.desc()
+    _check("sage_dequant", lib().sage_dequant(ctypes.byref(d), _ptr(w), _stream(stream)))
+    return w
+
+
+def gemv_workspace_bytes(p: Packed) -> int:
+    n = ctypes.c_size_t(0)
+    d = p.desc()
+    _check("sage_gemv_workspace_bytes", lib().sage_gemv_workspace_bytes(ctypes.byref(d), ctypes.byref(n)))
+    return n.value
+
+
+def workspace(nbytes: int, device):
+    """A zero-filled workspace (libsage keeps it zero-ready between calls)."""
+    torch = _torch()
+    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def gemv(p: Packed, x, y=None, ws=None, stream=None):
+    torch = _torch()
+    _require_cuda(x)
+    if y is None:
+        y = torch.empty(p.d_out, dtype=torch.float16, device=x.device)
+    if ws is None:
+        ws = workspace(gemv_workspace_bytes(p), x.device)
+    d = p.desc()
+    _check("sage_gemv", lib().sage_gemv(ctypes.byref(d), _ptr(x), _ptr(y), _ptr(ws), ws.numel(),
+                                        _stream(stream)))
+    return y
+
+
+def _mat_array(ps: Sequence[Packed]):
+    arr = (SageMatrix * len(ps))()
+    for i, p in enumerate(ps):
+        arr[i] = p.desc()
+    return arr
+
+
+def gemv_multi_workspace_bytes(ps: Sequence[Packed]) -> int:
+    n = ctypes.c_size_t(0)
+    arr = _mat_array(ps)
+    _check("sage_gemv_multi_workspace_bytes",
+           lib().sage_gemv_multi_workspace_bytes(arr, len(ps), ctypes.byref(n)))
+    return n.value
+
+
+def gemv_multi(ps: Sequence[Packed], xs, ys=None, ws=None, stream=None):
+    torch = _torch()
+    if ys is None:
+        ys = [torch.empty(p.d_out, dtype=torch.float16, device=x.device) for p, x in zip(ps, xs)]
+    if ws is None:
+        ws = workspace(gemv_multi_workspace_bytes(ps), xs[0].device)
+    arr = _mat_array(ps)
+    xa = (ctypes.c_void_p * len(ps))(*[_ptr(x) for x in xs])
+    ya = (ctypes.c_void_p * len(ps))(*[_ptr(y) for y in ys])
+    _check("sage_gemv_multi", lib().sage_gemv_multi(arr, xa, ya, len(ps), _ptr(ws), ws.numel(),
+                                                    _stream(stream)))
+    return ys
+
+
+def gemm_small_workspace_bytes(p: Packed, M: int) -> int:
+    n = ctypes.c_size_t(0)
+    d = p.desc()
+    _check("sage_gemm_small_workspace_bytes",
+           lib().sage_gemm_small_workspace_bytes(ctypes.byref(d), M, ctypes.byref(n)))
+    return n.value
+
+
+def gemm_small(p: Packed, X, Y=None, ws=None, stream=None):
+    torch = _torch()
+    _require_cuda(X)
+    M = X.shape[0]
+    if Y is None:
+        Y = torch.empty((M, p.d_out), dtype=torch.float16, device=X.device)
+    if ws is None:
+        ws = workspace(gemm_small_workspace_bytes(p, M), X.device)
+    d = p.desc()
+    _check("sage_gemm_small", lib().sage_gemm_small(ctypes.byref(d), _ptr(X), M, X.stride(0),
+                                                    _ptr(Y), Y.stride(0), _ptr(ws), ws.numel(),
+                                                    _stream(stream)))
+    return Y
+
+
+def expert_table(experts: Sequence[Sequence[Packed]], device):
+    """Device array of descriptors, expert e's matrix j at e*n_mats + j (for moe_gemv)."""
+    torch = _torch()
+    n_mats = len(experts[0])
+    flat = [m for ex in experts for m in ex]
+    arr = _mat_array(flat)
+    raw = bytes(arr)
+    host = torch.frombuffer(bytearray(raw), dtype=torch.uint8)
+    return host.to(device), n_mats
+
+
+def moe_gemv_workspace_bytes(shapes: Sequence[tuple], n_sel: int) -> int:
+    n = ctypes.c_size_t(0)
+    arr = (SageMatrix * len(shapes))(*[SageMatrix(o, i, 0, 0, None, None, None) for o, i in shapes])
+    _check("sage_moe_gemv_workspace_bytes",
+           lib().sage_moe_gemv_workspace_bytes(arr, len(shapes), n_sel, ctypes.byref(n)))
+    return n.value
+
+
+def moe_gemv(table, n_experts: int, shapes: Sequence[tuple], ids, xs, x_strides, ys, y_strides,
+             ws=None, stream=None):
+    """Grouped products over routed experts (see sage_moe_gemv in include/sage.h)."""
+    _require_cuda(table, ids)
+    n_mats = len(shapes)
+    if ws is None:
+        ws = workspace(moe_gemv_workspace_bytes(shapes, ids.numel()), ids.device)
+    sh = (SageMatrix * n_mats)(*[SageMatrix(o, i, 0, 0, None, None, None) for o, i in shapes])
+    xa = (ctypes.c_void_p * n_mats)(*[_ptr(x) for x in xs])
+    ya = (ctypes.c_void_p * n_mats)(*[_ptr(y) for y in ys])
+    xsa = (ctypes.c_int64 * n_mats)(*x_strides)
+    ysa = (ctypes.c_int64 * n_mats)(*y_strides)
+    _check("sage_moe_gemv", lib().sage_moe_gemv(
+        ctypes.cast(_ptr(table), _PM), n_experts, sh, n_mats, _ptr(ids), ids.numel(), xa, xsa,
+        ya, ysa, _ptr(ws), ws.numel(), _stream(stream)))
+    return ys

@@ -1,0 +1,538 @@
+// Batch-one decode-and-multiply for SAGE-packed weights on gfx950 (SAGE paper §3.5 and App. A.1).
+//
+// Work decomposition. Lane l of a wavefront owns output row 64*rt + l of one row tile; the four
+// wavefronts of a workgroup own four consecutive row tiles and share one range of column groups
+// (split-K over workgroups when the matrix alone does not fill the GPU, App. A.1 / §3.5). Because
+// every lane of a wave works on the same input columns at the same time, the activations are
+// uniform across the wave and no cross-lane reduction is needed.
+//
+// Per workgroup set-up, in LDS:
+//   * the codebook, replicated 16 times with replica r at byte offset 16 r of each 256-byte row,
+//     so lane l reads replica (l mod 16): random codeword gathers become bank-conflict free;
+//   * the permuted activations x[pi[p]] of the workgroup's columns (gathered once, §3.2/§3.5);
+//   * for every subvector position, a table of the 16 sign patterns of each 4-wide activation
+//     half: entry n holds (x0..x3) and (x4..x7) with element i negated when bit i of n is set.
+// A subvector is then: two conflict-free 8-byte table reads selected by the low and high sign
+// nibbles, one 16-byte codeword read, four fp16 dot2 steps with fp32 accumulation, and the radius
+// mu + q*delta applied once to the 8-term dot product (App. A.1 applies the radius after the dot
+// for the same reason: one multiply instead of eight).
+//
+// Split-K partials go to a caller workspace; the last workgroup of a row-tile group (atomic
+// counter) sums them in split order, writes y in fp16 and resets the counter to zero.
+#include "sage_internal.hpp"
+#include "sage_gemv.hpp"
+
+namespace sage {
+namespace {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ inline uint4 ld_stream16(const uint8_t* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ inline uint2 ld_stream8(const uint8_t* p) {
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(v.x, v.y);
+}
+
+// First step of a dot chain, accumulator 0 (VOP3P form, so no register needs zeroing first).
+__device__ inline float dot2_z(uint32_t a, uint32_t b) {
+  float r;
+  asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ inline float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
+                                false);
+}
+
+// Sign pattern n applied to four fp16 values held as two packed dwords.
+__device__ inline uint2 apply_nibble(uint32_t p01, uint32_t p23, uint32_t n) {
+  const uint32_t m01 = ((n & 1u) << 15) | ((n & 2u) << 30);
+  const uint32_t m23 = ((n & 4u) << 13) | ((n & 8u) << 28);
+  return make_uint2(p01 ^ m01, p23 ^ m23);
+}
+
+// (a & m) | c in one VALU op with m in an SGPR and c in a VGPR (register-only inline asm).
+__device__ inline uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(c));
+  return r;
+}
+// ((a >> 8) & m) in one VALU op (SDWA byte select; the compiler only forms the 16/24-bit cases).
+__device__ inline uint32_t and_byte1(uint32_t a, uint32_t m) {
+  uint32_t r;
+  asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1 "
+      "src1_sel:DWORD"
+      : "=v"(r)
+      : "v"(a), "s"(m));
+  return r;
+}
+
+// Compile-time constants and LDS layout of one split (L = log2 K).
+template <int L>
+struct SplitC {
+  static constexpr uint32_t kK = 1u << L;
+  static constexpr uint32_t kZMask = (kK - 1u) << 8;                      // F at bit 8
+  static constexpr uint32_t kQMask = ((1u << (10 - L)) - 1u) << (8 + L);  // q at bit 8 + L
+  // OR-ing this exponent onto q at bit 8+L gives the float 2^(15-L) + q exactly.
+  static constexpr uint32_t kExpo = (127u + 15u - (uint32_t)L) << 23;
+  static constexpr float kBias = (float)(1u << (15 - L));
+  // LDS: codebook replicas and signed-activation tables at compile-time offsets, so that every
+  // table offset folds into the ds_read immediate. K = 256 needs the tables first.
+  static constexpr int kCbOff = (L == 8) ? 32768 : 0;
+  static constexpr int kXtOff = (L == 8) ? 0 : (int)(kK * 256);
+};
+
+struct Resolved {
+  const uint8_t* packed;
+  const uint16_t* codebook;
+  const int32_t* pi;
+  int L;
+};
+
+template <int L>
+__device__ inline int xp_offset(int gs) {
+  return (L == 8) ? 32768 + 65536 : SplitC<L>::kXtOff + gs * kSubPerGroup * 256;
+}
+
+struct GroupRegs {
+  uint32_t p[8];
+  uint32_t x, g;
+};
+
+__device__ inline void load_group(GroupRegs& r, const uint8_t* blk, int lane) {
+  const uint4 a = ld_stream16(blk + kPlaneA + lane * 16);
+  const uint4 b = ld_stream16(blk + kPlaneB + lane * 16);
+  const uint2 s = ld_stream8(blk + kSidePlane + lane * 8);
+  r.p[0] = a.x; r.p[1] = a.y; r.p[2] = a.z; r.p[3] = a.w;
+  r.p[4] = b.x; r.p[5] = b.y; r.p[6] = b.z; r.p[7] = b.w;
+  r.x = s.x;
+  r.g = s.y;
+}
+
+// LDS reads at absolute LDS byte addresses. The kernel declares no static LDS, so its dynamic LDS
+// starts at address 0 and table offsets become ds_read immediates.
+typedef __attribute__((address_space(3))) const u32x2 lds_u2;
+typedef __attribute__((address_space(3))) const u32x4 lds_u4;
+__device__ inline uint2 lds8(uint32_t addr) {
+  const u32x2 v = *(lds_u2*)(size_t)addr;
+  return make_uint2(v.x, v.y);
+}
+__device__ inline uint4 lds16(uint32_t addr) {
+  const u32x4 v = *(lds_u4*)(size_t)addr;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// One subvector: two signed-activation half reads, one codeword read, 4 dot2, radius, accumulate.
+template <int L>
+__device__ __forceinline__ float subvec(int xt_off, uint32_t lo, uint32_t hi, uint32_t cz,
+                                        uint32_t qbits, float dl, float mu_b, float acc) {
+  const uint2 x0 = lds8(lo + (uint32_t)xt_off);
+  const uint2 x1 = lds8(hi + (uint32_t)(xt_off + 8));
+  const uint4 c = lds16(cz + (uint32_t)SplitC<L>::kCbOff);
+  float t = dot2_z(c.x, x0.x);
+  t = dot2(c.y, x0.y, t);
+  t = dot2(c.z, x1.x, t);
+  t = dot2(c.w, x1.y, t);
+  const float r = fmaf(__uint_as_float(qbits), dl, mu_b);
+  return fmaf(r, t, acc);
+}
+
+// All 16 subvectors of one group; k is the group's slot in this workgroup (compile-time).
+template <int L, int k>
+__device__ __forceinline__ float group_dot(const GroupRegs& R, uint32_t laneoff, uint32_t expo,
+                                           float acc) {
+  using C = SplitC<L>;
+  const float mu = h2f(R.g);
+  const float dl = h2f(R.g >> 16);
+  const float mu_b = fmaf(-C::kBias, dl, mu);  // radius = (2^(15-L) + q) * delta + mu_b
+  const uint32_t x4 = R.x << 4;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t P = R.p[i];
+    const int off_a = C::kXtOff + k * kSubPerGroup * 256 + (2 * i) * 256;
+    // subvector a = 2i: nibbles at bits 4..7 and 28..31, field at bit 8
+    acc = subvec<L>(off_a, P & 0xF0u, (P >> 24) & 0xF0u, and_or(P, C::kZMask, laneoff),
+                    and_or(P, C::kQMask, expo), dl, mu_b, acc);
+    // subvector b = 2i+1: nibble at bits 0..3 of P and slot i of X, field at bit 18
+    uint32_t hi_b;
+    if (i & 1) {
+      const int byte = (i - 1) >> 1;
+      hi_b = byte == 0 ? (R.x & 0xF0u)
+           : byte == 1 ? and_byte1(R.x, 0xF0u)
+           : byte == 2 ? ((R.x >> 16) & 0xF0u) : ((R.x >> 24) & 0xF0u);
+    } else {
+      const int byte = i >> 1;
+      hi_b = byte == 0 ? (x4 & 0xF0u)
+           : byte == 1 ? and_byte1(x4, 0xF0u)
+           : byte == 2 ? ((x4 >> 16) & 0xF0u) : ((x4 >> 24) & 0xF0u);
+    }
+    const uint32_t Pb = P >> 10;
+    acc = subvec<L>(off_a + 256, (P << 4) & 0xF0u, hi_b, and_or(Pb, C::kZMask, laneoff),
+                    and_or(Pb, C::kQMask, expo), dl, mu_b, acc);
+  }
+  return acc;
+}
+
+template <int L>
+__device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int inst, int wgrow,
+                                          int split, uint8_t* smem) {
+  using C = SplitC<L>;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int g0 = split * J.gs;
+  const int ngl = min(J.ng - g0, J.gs);
+  const int rt = wgrow * kGemvWaves + wave;
+  const bool tile_ok = rt < J.rt;
+
+  // 1. Issue this wave's packed loads for its first two groups before the LDS set-up; later
+  //    groups stream through a three-deep register ring (two groups in flight while one computes).
+  GroupRegs ring[3];
+  const uint8_t* blk0 = R.packed + ((int64_t)rt * J.ng + g0) * kBlockBytes;
+  if (tile_ok) {
+    if (ngl > 0) load_group(ring[0], blk0, lane);
+    if (ngl > 1) load_group(ring[1], blk0 + kBlockBytes, lane);
+  }
+
+  // 2. LDS set-up: replicated codebook, gathered activations, signed-activation tables.
+  uint16_t* xp = reinterpret_cast<uint16_t*>(smem + xp_offset<L>(J.gs));
+  {
+    const uint4* cbg = reinterpret_cast<const uint4*>(R.codebook);
+    for (int e = tid; e < (int)C::kK * 16; e += kGemvThreads)
+      *reinterpret_cast<uint4*>(smem + C::kCbOff + (e >> 4) * 256 + (e & 15) * 16) = cbg[e >> 4];
+    const uint16_t* x = J.x + (int64_t)inst * J.x_stride;
+    const int c0 = g0 * kGroupCols;
+    for (int p = tid; p < ngl * kGroupCols; p += kGemvThreads) {
+      const int col = c0 + p;
+      xp[p] = x[R.pi ? R.pi[col] : col];
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < ngl * kSubPerGroup * 16; e += kGemvThreads) {
+    const int step = e >> 4;
+    const uint32_t n = (uint32_t)(e & 15);
+    const uint4 v = *reinterpret_cast<const uint4*>(xp + step * 8);
+    const uint2 lo = apply_nibble(v.x, v.y, n);
+    const uint2 hi = apply_nibble(v.z, v.w, n);
+    *reinterpret_cast<uint4*>(smem + C::kXtOff + step * 256 + n * 16) =
+        make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
+  __syncthreads();
+
+  // 3. Decode and multiply.
+  float acc = 0.0f;
+  const uint32_t laneoff = (uint32_t)(lane & 15) * 16u;
+  const uint32_t expo = C::kExpo;
+  if (tile_ok) {
+#define SAGE_GROUP(k)                                                              \
+    if (k < ngl) {                                                                 \
+      if (k + 2 < ngl) load_group(ring[(k + 2) % 3], blk0 + (k + 2) * kBlockBytes, lane); \
+      acc = group_dot<L, k>(ring[k % 3], laneoff, expo, acc);                      \
+    }
+    SAGE_GROUP(0) SAGE_GROUP(1) SAGE_GROUP(2) SAGE_GROUP(3)
+    SAGE_GROUP(4) SAGE_GROUP(5) SAGE_GROUP(6) SAGE_GROUP(7)
+#undef SAGE_GROUP
+  }
+
+  // 4. Output: direct, or split-K partials reduced by the last workgroup of the row-tile group.
+  const int row = rt * kTileRows + lane;
+  const bool row_ok = tile_ok && row < J.d_out;
+  uint16_t* y = J.y + (int64_t)inst * J.y_stride;
+  if (J.S == 1) {
+    if (row_ok) y[row] = f2h(acc);
+    return;
+  }
+  float* part = J.partial + (int64_t)inst * J.partial_stride;
+  const int64_t rows_pad = (int64_t)J.rt * kTileRows;
+  if (row_ok) part[(int64_t)split * rows_pad + row] = acc;
+  __threadfence();
+  __syncthreads();
+  uint32_t* flag = reinterpret_cast<uint32_t*>(smem);  // LDS no longer needed
+  uint32_t* counter = J.counters + (int64_t)inst * J.counters_stride + wgrow;
+  if (tid == 0) *flag = (atomicAdd(counter, 1u) == (uint32_t)(J.S - 1)) ? 1u : 0u;
+  __syncthreads();
+  if (*flag == 0u) return;
+  __threadfence();
+  if (row_ok) {
+    float s = 0.0f;
+    for (int sp = 0; sp < J.S; ++sp) s += __builtin_nontemporal_load(part + sp * rows_pad + row);
+    y[row] = f2h(s);
+  }
+  if (tid == 0) atomicExch(counter, 0u);
+}
+
+__global__ void __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
+gemv_kernel(JobTable T) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int wg = blockIdx.x;
+  int jid = 0;
+  while (jid + 1 < T.n && wg >= T.jobs[jid + 1].wg_begin) ++jid;
+  const Job& J = T.jobs[jid];
+  int local = wg - J.wg_begin;
+  const int inst = local / J.wg_per_inst;
+  local -= inst * J.wg_per_inst;
+  const int wgrow = local / J.S;
+  const int split = local - wgrow * J.S;
+  Resolved R;
+  if (J.table != nullptr) {
+    const sage_matrix_t* M = J.table + (int64_t)J.ids[inst] * J.tstride + J.toff;
+    R.packed = static_cast<const uint8_t*>(M->packed);
+    R.codebook = M->codebook;
+    R.pi = M->pi;
+    R.L = M->log2K;
+  } else {
+    R.packed = J.packed;
+    R.codebook = J.codebook;
+    R.pi = J.pi;
+    R.L = J.log2K;
+  }
+  switch (R.L) {
+    case 4: gemv_body<4>(R, J, inst, wgrow, split, smem); break;
+    case 5: gemv_body<5>(R, J, inst, wgrow, split, smem); break;
+    case 6: gemv_body<6>(R, J, inst, wgrow, split, smem); break;
+    case 7: gemv_body<7>(R, J, inst, wgrow, split, smem); break;
+    default: gemv_body<8>(R, J, inst, wgrow, split, smem); break;
+  }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------------------------------
+// Host planning
+
+size_t lds_bytes(int maxL, int gs) {
+  // the largest layout among the splits a launch may meet (see SplitC / xp_offset)
+  size_t need = 0;
+  for (int L = 4; L <= maxL; ++L) {
+    const size_t b = (L == 8) ? (size_t)32768 + 65536 + (size_t)gs * kGroupCols * 2
+                              : ((size_t)1 << L) * 256 + (size_t)gs * kSubPerGroup * 256 +
+                                    (size_t)gs * kGroupCols * 2;
+    if (b > need) need = b;
+  }
+  return need;
+}
+
+int plan_groups_per_split(int64_t total_blocks) {
+  // About 2.5 workgroups of 4 row tiles per compute unit; more groups per split when the work is
+  // large enough, so the LDS set-up is amortised over more blocks.
+  const int64_t target_wg = (int64_t)device_cu_count() * 5 / 2;
+  int64_t gs = total_blocks / (kGemvWaves * target_wg);
+  if (gs < 1) gs = 1;
+  if (gs > kMaxGroupsPerSplit) gs = kMaxGroupsPerSplit;
+  return (int)gs;
+}
+
+void plan_job(Job& J, int d_out, int d_in, int gs_hint, int instances) {
+  J.d_out = d_out;
+  J.d_in = d_in;
+  J.rt = ceil_div(d_out, kTileRows);
+  J.ng = d_in / kGroupCols;
+  J.wgr = ceil_div(J.rt, kGemvWaves);
+  J.gs = gs_hint < J.ng ? gs_hint : J.ng;
+  J.S = ceil_div(J.ng, J.gs);
+  J.gs = ceil_div(J.ng, J.S);
+  J.wg_per_inst = J.wgr * J.S;
+  J.inst = instances;
+  J.partial_stride = J.S > 1 ? (int64_t)J.S * J.rt * kTileRows : 0;
+  J.counters_stride = J.S > 1 ? J.wgr : 0;
+}
+
+size_t job_workspace_bytes(const Job& J) {
+  if (J.S == 1) return 0;
+  const size_t per = (size_t)J.partial_stride * 4 + (size_t)J.counters_stride * 4;
+  return ((size_t)J.inst * per + 255) / 256 * 256;
+}
+
+int finish_and_launch(JobTable& T, void* ws, size_t ws_bytes, hipStream_t stream, int maxL) {
+  size_t need = 0;
+  int wg = 0;
+  size_t lds = 0;
+  for (int i = 0; i < T.n; ++i) {
+    Job& J = T.jobs[i];
+    const size_t bytes = job_workspace_bytes(J);
+    if (bytes) {
+      if (ws == nullptr) return SAGE_ERR_WORKSPACE;
+      char* base = static_cast<char*>(ws) + need;
+      J.partial = reinterpret_cast<float*>(base);
+      J.counters = reinterpret_cast<uint32_t*>(base + (size_t)J.inst * J.partial_stride * 4);
+    } else {
+      J.partial = nullptr;
+      J.counters = nullptr;
+    }
+    need += bytes;
+    J.wg_begin = wg;
+    wg += J.wg_per_inst * J.inst;
+    const size_t l = lds_bytes(maxL, J.gs);
+    if (l > lds) lds = l;
+  }
+  if (need > ws_bytes) return SAGE_ERR_WORKSPACE;
+  if (need && !aligned(ws, 256)) return SAGE_ERR_ALIGN;
+  T.total_wg = wg;
+  if (wg == 0) return SAGE_OK;
+  static bool attr_done = false;
+  if (!attr_done) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
+      return SAGE_ERR_HIP;
+    attr_done = true;
+  }
+  hipLaunchKernelGGL(gemv_kernel, dim3(wg), dim3(kGemvThreads), lds, stream, T);
+  return hip_status();
+}
+
+size_t plan_workspace(const Job* jobs, int n) {
+  size_t need = 0;
+  for (int i = 0; i < n; ++i) need += job_workspace_bytes(jobs[i]);
+  return need;
+}
+
+}  // namespace sage
+
+using namespace sage;
+
+namespace {
+
+void direct_job(Job& J, const sage_matrix_t* m, int gs) {
+  J = Job{};
+  J.packed = static_cast<const uint8_t*>(m->packed);
+  J.codebook = m->codebook;
+  J.pi = m->pi;
+  J.log2K = m->log2K;
+  plan_job(J, m->d_out, m->d_in, gs, 1);
+}
+
+int gs_for(const sage_matrix_t* mats, int n) {
+  int64_t blocks = 0;
+  for (int i = 0; i < n; ++i)
+    blocks += (int64_t)ceil_div(mats[i].d_out, kTileRows) * (mats[i].d_in / kGroupCols);
+  return plan_groups_per_split(blocks);
+}
+
+}  // namespace
+
+extern "C" {
+
+int sage_gemv_workspace_bytes(const sage_matrix_t* m, size_t* bytes) {
+  if (bytes == nullptr) return SAGE_ERR_NULL;
+  int st = check_matrix(m);
+  if (st != SAGE_OK) return st;
+  Job J;
+  direct_job(J, m, gs_for(m, 1));
+  *bytes = job_workspace_bytes(J);
+  return SAGE_OK;
+}
+
+int sage_gemv(const sage_matrix_t* m, const uint16_t* x, uint16_t* y, void* ws, size_t ws_bytes,
+              sage_stream_t stream) {
+  const uint16_t* xs[1] = {x};
+  uint16_t* ys[1] = {y};
+  return sage_gemv_multi(m, xs, ys, 1, ws, ws_bytes, stream);
+}
+
+int sage_gemv_multi_workspace_bytes(const sage_matrix_t* mats, int n, size_t* bytes) {
+  if (bytes == nullptr || mats == nullptr) return SAGE_ERR_NULL;
+  if (n < 1 || n > kMaxJobs) return SAGE_ERR_ARG;
+  for (int i = 0; i < n; ++i) {
+    int st = check_matrix(&mats[i]);
+    if (st != SAGE_OK) return st;
+  }
+  const int gs = gs_for(mats, n);
+  size_t need = 0;
+  for (int i = 0; i < n; ++i) {
+    Job J;
+    direct_job(J, &mats[i], gs);
+    need += job_workspace_bytes(J);
+  }
+  *bytes = need;
+  return SAGE_OK;
+}
+
+int sage_gemv_multi(const sage_matrix_t* mats, const uint16_t* const* xs, uint16_t* const* ys,
+                    int n, void* ws, size_t ws_bytes, sage_stream_t stream) {
+  if (mats == nullptr || xs == nullptr || ys == nullptr) return SAGE_ERR_NULL;
+  if (n < 1 || n > kMaxJobs) return SAGE_ERR_ARG;
+  for (int i = 0; i < n; ++i) {
+    int st = check_matrix(&mats[i]);
+    if (st != SAGE_OK) return st;
+    if (xs[i] == nullptr || ys[i] == nullptr) return SAGE_ERR_NULL;
+    if (!aligned(xs[i], 4) || !aligned(ys[i], 2)) return SAGE_ERR_ALIGN;
+  }
+  JobTable T{};
+  T.n = n;
+  const int gs = gs_for(mats, n);
+  int maxL = 4;
+  for (int i = 0; i < n; ++i) {
+    direct_job(T.jobs[i], &mats[i], gs);
+    T.jobs[i].x = xs[i];
+    T.jobs[i].y = ys[i];
+    if (mats[i].log2K > maxL) maxL = mats[i].log2K;
+  }
+  return finish_and_launch(T, ws, ws_bytes, (hipStream_t)stream, maxL);
+}
+
+int sage_moe_gemv_workspace_bytes(const sage_matrix_t* shapes, int n_mats, int n_sel,
+                                  size_t* bytes) {
+  if (bytes == nullptr || shapes == nullptr) return SAGE_ERR_NULL;
+  if (n_mats < 1 || n_mats > kMaxJobs || n_sel < 1) return SAGE_ERR_ARG;
+  int64_t blocks = 0;
+  for (int j = 0; j < n_mats; ++j) {
+    int st = check_shape(shapes[j].d_out, shapes[j].d_in);
+    if (st != SAGE_OK) return st;
+    blocks += (int64_t)n_sel * ceil_div(shapes[j].d_out, kTileRows) * (shapes[j].d_in / kGroupCols);
+  }
+  const int gs = plan_groups_per_split(blocks);
+  size_t need = 0;
+  for (int j = 0; j < n_mats; ++j) {
+    Job J{};
+    plan_job(J, shapes[j].d_out, shapes[j].d_in, gs, n_sel);
+    need += job_workspace_bytes(J);
+  }
+  *bytes = need;
+  return SAGE_OK;
+}
+
+int sage_moe_gemv(const sage_matrix_t* experts_dev, int n_experts, const sage_matrix_t* shapes,
+                  int n_mats, const int32_t* ids_dev, int n_sel, const uint16_t* const* xs,
+                  const int64_t* x_strides, uint16_t* const* ys, const int64_t* y_strides,
+                  void* ws, size_t ws_bytes, sage_stream_t stream) {
+  if (experts_dev == nullptr || shapes == nullptr || ids_dev == nullptr || xs == nullptr ||
+      ys == nullptr || x_strides == nullptr || y_strides == nullptr)
+    return SAGE_ERR_NULL;
+  if (n_experts < 1 || n_mats < 1 || n_mats > kMaxJobs || n_sel < 1 || n_sel > n_experts)
+    return SAGE_ERR_ARG;
+  if (!aligned(experts_dev, 8) || !aligned(ids_dev, 4)) return SAGE_ERR_ALIGN;
+  int64_t blocks = 0;
+  for (int j = 0; j < n_mats; ++j) {
+    int st = check_shape(shapes[j].d_out, shapes[j].d_in);
+    if (st != SAGE_OK) return st;
+    if (xs[j] == nullptr || ys[j] == nullptr) return SAGE_ERR_NULL;
+    if (!aligned(xs[j], 4) || !aligned(ys[j], 2)) return SAGE_ERR_ALIGN;
+    if (x_strides[j] < 0 || (x_strides[j] & 1) || y_strides[j] < 0) return SAGE_ERR_ARG;
+    if (n_sel > 1 && y_strides[j] < shapes[j].d_out) return SAGE_ERR_ARG;
+    blocks += (int64_t)n_sel * ceil_div(shapes[j].d_out, kTileRows) * (shapes[j].d_in / kGroupCols);
+  }
+  const int gs = plan_groups_per_split(blocks);
+  JobTable T{};
+  T.n = n_mats;
+  for (int j = 0; j < n_mats; ++j) {
+    Job& J = T.jobs[j];
+    J = Job{};
+    J.table = experts_dev;
+    J.ids = ids_dev;
+    J.tstride = n_mats;
+    J.toff = j;
+    plan_job(J, shapes[j].d_out, shapes[j].d_in, gs, n_sel);
+    J.x = xs[j];
+    J.x_stride = x_strides[j];
+    J.y = ys[j];
+    J.y_stride = y_strides[j];
+  }
+  return finish_and_launch(T, ws, ws_bytes, (hipStream_t)stream, 8);
+}
+
+}  // extern "C"

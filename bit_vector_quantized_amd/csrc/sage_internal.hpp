@@ -1,0 +1,113 @@
+// Internal definitions shared by the libsage translation units (not part of the C ABI).
+//
+// Packed layout (format version 2). Rows are grouped in tiles of 64 (one wavefront lane per row);
+// columns in groups of 128 (16 subvectors of 8 weights: the radius-grid group of the SAGE paper,
+// §3.1 / App. A.6). Each (row tile, column group) block is 2560 bytes and blocks are stored
+// row-tile major: block(rt, g) at byte (rt * n_groups + g) * 2560. Inside a block:
+//
+//   bytes [   0, 1024)  plane A: lane l owns 16 bytes = payload dwords P0..P3 of row 64 rt + l
+//   bytes [1024, 2048)  plane B: lane l owns 16 bytes = payload dwords P4..P7
+//   bytes [2048, 2560)  side plane: lane l owns 8 bytes = dword X, then dword G = mu | delta << 16
+//
+// With s_j the sign byte of subvector j of the group (bit i <=> weight i negative), z_j its codeword
+// index, q_j its radius code and F_j = z_j | q_j << log2K (10 bits), payload dword P_i (i = 0..7)
+// carries the pair a = 2i, b = 2i + 1:
+//
+//   bits [ 0, 4)  s_b & 15        bits [ 8,18)  F_a          bits [28,32)  s_a >> 4
+//   bits [ 4, 8)  s_a & 15        bits [18,28)  F_b
+//
+// and X carries s_{2i+1} >> 4 at bits [4i, 4i+4). Every subvector thus costs 8 + log2K + V = 18
+// bits (§3.1 Eq. (3)) and every group 4 more bytes of fp16 grid. The positions are chosen for the
+// decode kernel: each sign nibble sits in bits 4..7 of some byte (one masked select gives 16x the
+// nibble, a table offset), F_a sits at bit 8 (one and-or gives the codeword's LDS row and, with an
+// exponent OR-ed in, q as a float), F_b reaches the same position with one shift. Rows past d_out
+// in the last tile are zero.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/sage.h"
+
+namespace sage {
+
+constexpr int kFormatVersion = 2;
+constexpr int kTileRows = 64;                  // rows per tile = lanes per wavefront
+constexpr int kGroupCols = 128;                // weights per radius-grid group
+constexpr int kSubPerGroup = 16;               // subvectors per group
+constexpr int kBlockBytes = 2560;              // 64 rows x 128 cols x 2.5 bits
+constexpr int kPlaneA = 0;
+constexpr int kPlaneB = 1024;
+constexpr int kSidePlane = 2048;
+
+// Pack / unpack one subvector pair of a payload dword (format version 2).
+__host__ __device__ inline uint32_t pack_pair(uint32_t sa, uint32_t sb, uint32_t fa, uint32_t fb) {
+  return (sb & 15u) | ((sa & 15u) << 4) | ((fa & 1023u) << 8) | ((fb & 1023u) << 18) |
+         ((sa >> 4) << 28);
+}
+// Reads the 8 payload dwords and X of (lane) in a block into p[0..7], returns X; G via *grid.
+__device__ inline uint32_t read_lane_payload(const uint8_t* blk, int lane, uint32_t p[8],
+                                             uint32_t* grid) {
+  const uint4 a = *reinterpret_cast<const uint4*>(blk + kPlaneA + lane * 16);
+  const uint4 b = *reinterpret_cast<const uint4*>(blk + kPlaneB + lane * 16);
+  const uint2 s = *reinterpret_cast<const uint2*>(blk + kSidePlane + lane * 8);
+  p[0] = a.x; p[1] = a.y; p[2] = a.z; p[3] = a.w;
+  p[4] = b.x; p[5] = b.y; p[6] = b.z; p[7] = b.w;
+  *grid = s.y;
+  return s.x;
+}
+// Sign byte, and 10-bit index/radius field of subvector j (0..15) from the payload and X.
+__device__ inline uint32_t sign_of(const uint32_t p[8], uint32_t x, int j) {
+  const uint32_t w = p[j >> 1];
+  return (j & 1) ? ((w & 15u) | (((x >> (4 * (j >> 1))) & 15u) << 4))
+                 : (((w >> 4) & 15u) | ((w >> 28) << 4));
+}
+__device__ inline uint32_t field_of(const uint32_t p[8], int j) {
+  return (p[j >> 1] >> ((j & 1) ? 18 : 8)) & 1023u;
+}
+
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+inline int check_split(int log2K, int V) {
+  if (log2K < 4 || log2K > 8 || log2K + V != 10) return SAGE_ERR_SPLIT;
+  return SAGE_OK;
+}
+
+inline int check_shape(int d_out, int d_in) {
+  if (d_out < 1 || d_in < kGroupCols || d_in % kGroupCols != 0) return SAGE_ERR_SHAPE;
+  // keep every byte offset inside 63 bits and every row index inside int32
+  if ((int64_t)d_out * (int64_t)d_in > ((int64_t)1 << 40)) return SAGE_ERR_SHAPE;
+  return SAGE_OK;
+}
+
+inline size_t packed_bytes(int d_out, int d_in) {
+  return (size_t)ceil_div(d_out, kTileRows) * (size_t)(d_in / kGroupCols) * kBlockBytes;
+}
+
+int check_matrix(const sage_matrix_t* m);   // shape, split, pointers, alignment
+int hip_status();                            // SAGE_ERR_HIP if the last launch failed
+int device_cu_count();                       // compute units of the current device (cached)
+
+// fp16 <-> fp32 on bit patterns; the float -> half conversion rounds to nearest even.
+__device__ inline float h2f(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits16 & 0xFFFFu));
+}
+__device__ inline uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+// fp64 -> fp16 with a single round-to-nearest-even: round to fp32 "to odd" first (exact when the
+// fp32 rounding was exact), then RNE to fp16. Rounding to odd with >= 2 extra bits of precision
+// makes the second rounding equal to a direct correct rounding.
+__device__ inline uint16_t f64_to_f16_rne(double d) {
+  float f = (float)d;
+  if ((double)f != d) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 1u) == 0u) u += (fabs((double)f) < fabs(d)) ? 1u : 0xFFFFFFFFu;
+    f = __uint_as_float(u);
+  }
+  return f2h(f);
+}
+
+}  // namespace sage

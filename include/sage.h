@@ -1,0 +1,180 @@
+/*
+ * sage.h -- C ABI of libsage, the MI355X (gfx950) decode library for SAGE's 2.25-bit spherical
+ * vector-quantised weights.
+ *
+ * Method: "SAGE: Pushing 2-Bit Vector-Quantized LLMs toward Real-World Usability".
+ *   - Every row of a d_out x d_in weight is cut into subvectors of 8 consecutive weights along the
+ *     input axis (§3.1). A subvector stores 8 sign bits, a log2(K)-bit index z into a per-matrix
+ *     codebook of K nonnegative unit directions, and a V-bit radius code q (§3.1, Eq. (3):
+ *     8 + log2(K) + V = 18 bits).
+ *   - Every 128 weights of a row (16 consecutive subvectors) share an fp16 radius grid, offset mu
+ *     and step delta; the decoded radius is mu + q*delta (§3.1 Eq. (2); fp16 grid: App. A.6).
+ *   - The decoded weight is radius * (signs (.) c_z) (§3.1 Eq. (1)).
+ *   - Columns are stored in the ESG-permuted order pi (§3.2 Eq. (5)); at inference the input
+ *     vector is gathered through pi (§3.2, §3.5).
+ *   - The supported (K, V) splits are the five with log2(K) + V = 10 and 16 <= K <= 256 (the
+ *     paper's ABS candidates (64,4), (128,3), (256,2) of §3.3 Eq. (7), plus (16,6) and (32,5)).
+ *
+ * Conventions shared by every entry point
+ *   - All array arguments are DEVICE pointers owned by the caller; the library never allocates,
+ *     frees or retains them. Host pointers are only the descriptor arguments (sage_matrix_t*,
+ *     size_t*), read before the call returns.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream). Buffers must
+ *     stay valid until the work queued on that stream has completed. No call synchronises.
+ *   - fp16 data is passed as uint16_t bit patterns (IEEE binary16).
+ *   - Field arrays use permuted column order (the order of storage); x and y use original order.
+ *   - Return value: SAGE_OK (0) or one of the error codes below. Arguments are validated on the
+ *     host before anything is queued; an invalid call queues nothing. Data-dependent faults
+ *     (idx >= K, an out-of-range permutation entry or expert id) are not checked on the device
+ *     and give undefined results.
+ *   - Thread safety: calls may be made from several host threads. Calls that overlap on the same
+ *     stream run in order; concurrent calls that share an output or workspace buffer race.
+ */
+#ifndef SAGE_H
+#define SAGE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* sage_stream_t; /* a hipStream_t */
+
+enum sage_status {
+  SAGE_OK = 0,
+  SAGE_ERR_NULL = 1,      /* a required pointer argument is NULL */
+  SAGE_ERR_SHAPE = 2,     /* d_out < 1, d_in < 128, d_in % 128 != 0, M < 1, bad leading dims */
+  SAGE_ERR_SPLIT = 3,     /* log2K outside [4, 8] or log2K + V != 10 */
+  SAGE_ERR_ALIGN = 4,     /* a pointer does not have the alignment stated for it */
+  SAGE_ERR_WORKSPACE = 5, /* workspace pointer NULL or smaller than required */
+  SAGE_ERR_HIP = 6,       /* the HIP runtime reported an error while queueing */
+  SAGE_ERR_ARG = 7        /* any other invalid argument (counts, strides, ids) */
+};
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* sage_status_string(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH; packed-format version as a separate number.
+ * A packed buffer written by one format version is only readable by the same version. */
+int sage_version(void);
+int sage_format_version(void);
+
+/*
+ * A quantised matrix as the decode kernels read it.
+ *   d_out, d_in  weight shape (rows are outputs); d_in is a multiple of 128.
+ *   log2K, V     the split: K = 2^log2K codewords, V radius bits, log2K + V = 10.
+ *   packed       device buffer written by sage_pack (payload + fp16 grids), 256-byte aligned,
+ *                sage_packed_bytes() bytes.
+ *   codebook     device fp16 [K][8], codeword k at codebook + 8k, 16-byte aligned.
+ *   pi           device int32 [d_in]: pi[p] is the original input channel at permuted position p
+ *                (the gather form of §3.2 Eq. (5)). NULL means the identity permutation.
+ * The struct is plain data and may also live in device memory (see sage_moe_gemv).
+ */
+typedef struct sage_matrix {
+  int32_t d_out;
+  int32_t d_in;
+  int32_t log2K;
+  int32_t V;
+  const void* packed;
+  const uint16_t* codebook;
+  const int32_t* pi;
+} sage_matrix_t;
+
+/* Bytes of the packed buffer for a matrix (host only; no device work). */
+int sage_packed_bytes(int d_out, int d_in, int log2K, int V, size_t* bytes);
+
+/*
+ * sage_pack: re-lay the separate code fields of a matrix into the packed streaming layout.
+ *   signs  uint8 [d_out][d_in/8]   bit i set <=> weight i of the subvector is negative (§3.1)
+ *   idx    uint8 [d_out][d_in/8]   codeword index z, must be < K (§3.1, Eq. (1))
+ *   rcode  uint8 [d_out][d_in/8]   radius code q, must be < 2^V (§3.1, Eq. (2))
+ *   mu     fp16  [d_out][d_in/128] grid offset per 128-weight group (§3.1 Eq. (2), App. A.6)
+ *   delta  fp16  [d_out][d_in/128] grid step per 128-weight group
+ *   packed output, 256-byte aligned, sage_packed_bytes() bytes; fully overwritten (row padding
+ *          included).
+ * Bits of idx/rcode above log2K / V are ignored.
+ */
+int sage_pack(const uint8_t* signs, const uint8_t* idx, const uint8_t* rcode, const uint16_t* mu,
+              const uint16_t* delta, int d_out, int d_in, int log2K, int V, void* packed,
+              sage_stream_t stream);
+
+/* sage_unpack: the exact inverse of sage_pack, writing the same five field arrays. */
+int sage_unpack(const void* packed, int d_out, int d_in, int log2K, int V, uint8_t* signs,
+                uint8_t* idx, uint8_t* rcode, uint16_t* mu, uint16_t* delta, sage_stream_t stream);
+
+/*
+ * sage_dequant: dense fp16 copy of the decoded weights (a QDQ reference), original column order.
+ *   w  fp16 [d_out][d_in], row-major, 4-byte aligned. Each entry is the decoded weight
+ *      (mu + q*delta) * (+-c_z,i) of §3.1 Eq. (1)-(2) rounded once to nearest-even fp16, scattered
+ *      to column pi[p] (§3.2).
+ */
+int sage_dequant(const sage_matrix_t* m, uint16_t* w, sage_stream_t stream);
+
+/*
+ * sage_gemv: y = W_hat x for one input vector (batch one), the decode step of §3.5 / App. A.1.
+ *   x   fp16 [d_in], original channel order (the kernel gathers it through pi), 4-byte aligned.
+ *   y   fp16 [d_out], 2-byte aligned; written, not accumulated.
+ *   ws  workspace of at least sage_gemv_workspace_bytes() bytes, 256-byte aligned. It must be
+ *       zero-filled before its first use; every call leaves it ready for the next call (its
+ *       counters return to zero). A workspace must not be shared by calls that can overlap.
+ *       May be NULL when the required size is 0.
+ * Accumulation is fp32; the result is rounded once to fp16.
+ */
+int sage_gemv_workspace_bytes(const sage_matrix_t* m, size_t* bytes);
+int sage_gemv(const sage_matrix_t* m, const uint16_t* x, uint16_t* y, void* ws, size_t ws_bytes,
+              sage_stream_t stream);
+
+/*
+ * sage_gemv_multi: several independent products y_j = W_j x_j in one launch (for example the
+ * q/k/v or gate/up projections that read the same input). mats, xs and ys are HOST arrays of
+ * n entries; the pointers inside are device pointers with the alignments of sage_gemv. The
+ * workspace requirement is sage_gemv_multi_workspace_bytes() for the same list.
+ */
+int sage_gemv_multi_workspace_bytes(const sage_matrix_t* mats, int n, size_t* bytes);
+int sage_gemv_multi(const sage_matrix_t* mats, const uint16_t* const* xs, uint16_t* const* ys,
+                    int n, void* ws, size_t ws_bytes, sage_stream_t stream);
+
+/*
+ * sage_gemm_small: Y = X W_hat^T for a few activation rows (the small-batch / prefill path of
+ * §3.5 and App. A.1, where each decoded weight is reused across the rows).
+ *   X   fp16 [M][ldx] row-major, original channel order, ldx >= d_in, ldx even, 4-byte aligned.
+ *   Y   fp16 [M][ldy] row-major, ldy >= d_out.
+ *   M   >= 1. Any M is accepted; the kernels are tuned for M <= 64.
+ *   ws  as for sage_gemv, size from sage_gemm_small_workspace_bytes().
+ */
+int sage_gemm_small_workspace_bytes(const sage_matrix_t* m, int M, size_t* bytes);
+int sage_gemm_small(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, uint16_t* Y,
+                    int ldy, void* ws, size_t ws_bytes, sage_stream_t stream);
+
+/*
+ * sage_moe_gemv: grouped batch-one products over routed experts in one launch.
+ *   experts_dev  DEVICE array [n_experts * n_mats] of sage_matrix_t, 8-byte aligned; expert e's
+ *                matrix j is entry e*n_mats + j. Splits, codebooks, permutations and packed
+ *                buffers may differ per expert; the shape of matrix j must equal shapes[j] for
+ *                every expert (the device copy's d_out/d_in are not read).
+ *   shapes       HOST array [n_mats]; only d_out and d_in of each entry are used.
+ *   ids_dev      DEVICE int32 [n_sel], 4-byte aligned: the routed experts, each in [0, n_experts).
+ *   xs, ys       HOST arrays [n_mats] of DEVICE fp16 pointers. Slot s of matrix j reads
+ *                xs[j] + s*x_strides[j] (a stride of 0 shares one input, e.g. the token for
+ *                gate/up) and writes ys[j] + s*y_strides[j] (d_out[j] values).
+ *   x_strides, y_strides  HOST int64 [n_mats], in elements; x strides even, y strides >= d_out
+ *                when n_sel > 1.
+ *   ws           workspace of sage_moe_gemv_workspace_bytes() bytes, zero-filled before first use
+ *                (kept zero-ready across calls, as for sage_gemv).
+ * One launch covers a mixture-of-experts layer's routed matrices (gate/up on the shared token,
+ * down on each expert's own intermediate vector); the router's combine stays with the caller.
+ */
+int sage_moe_gemv_workspace_bytes(const sage_matrix_t* shapes, int n_mats, int n_sel,
+                                  size_t* bytes);
+int sage_moe_gemv(const sage_matrix_t* experts_dev, int n_experts, const sage_matrix_t* shapes,
+                  int n_mats, const int32_t* ids_dev, int n_sel, const uint16_t* const* xs,
+                  const int64_t* x_strides, uint16_t* const* ys, const int64_t* y_strides,
+                  void* ws, size_t ws_bytes, sage_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAGE_H */
