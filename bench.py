@@ -1,0 +1,442 @@
+#!/usr/bin/env python3
+"""Benchmark of the SAGE batch-one decode path on one MI355X.
+
+Default workload: one Qwen3-4B-shaped decoder layer at batch one (q 4096x2560, k/v 1024x2560,
+o 2560x4096, gate/up 9728x2560, down 2560x9728), split (K, V) = (64, 4), codes drawn directly
+(synthetic, seeded). A step is one pass over the layer's seven projections in dependency order:
+q|k|v in one launch (they read the same input), o, gate|up in one launch, down. Every step uses a
+different copy of the layer's packed weights, and the copies together exceed 512 MB, twice the
+MI355X's 256 MB last-level cache, so weights stream from HBM as they would in a model.
+
+The timed region replays a HIP graph of the steps (launching from Python per kernel would measure
+the host, not the GPU). It prints one JSON line: whole-step packed-weight GB/s (the metric), the
+per-step time, tokens/s of the layer, the roofline of the dominant kernel (the gate|up launch)
+from HIP events recorded around that launch on its stream (enqueued behind a device sleep, so the
+host's launch cost stays hidden; graphs cannot carry timing events on HIP), and the CPU oracle's
+rate on a bounded sample of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--workload layer|sweep|gemm|moe|single]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import glob
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16, published
+MALL_BYTES = 256 << 20
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="layer",
+                    choices=["layer", "sweep", "gemm", "moe", "single", "all"])
+    ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--eager", action="store_true", help="launch from Python (no graph)")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------------------------------------
+# inputs on the device (seeded synthetic fields, packed by libsage)
+# ------------------------------------------------------------------------------------------------
+
+def upload_pack(c):
+    import numpy as np
+    import torch
+    import bit_vector_quantized_amd as sage
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    L = int(c.K).bit_length() - 1
+    return sage.pack(t(c.signs), t(c.idx), t(c.rcode), t(c.mu.view(np.float16)),
+                     t(c.delta.view(np.float16)), t(c.codebook.view(np.float16)), t(c.pi), L, c.V)
+
+
+def clone_packed(p):
+    import bit_vector_quantized_amd as sage
+    return sage.Packed(p.d_out, p.d_in, p.log2K, p.V, p.packed.clone(), p.codebook.clone(),
+                       None if p.pi is None else p.pi.clone())
+
+
+def algorithmic_bytes(p, n_x=1):
+    """payload + fp16 grid + codebook + pi (int32) + x + y of one product (SAGE's stored fields
+    and the fp16 vectors), the per-unit traffic a perfect kernel reads or writes once."""
+    packed = p.d_out * p.d_in * 18 // 64 + p.d_out * (p.d_in // 128) * 4
+    return packed + (1 << p.log2K) * 16 + (p.d_in * 4 if p.pi is not None else 0) \
+        + n_x * p.d_in * 2 + p.d_out * 2
+
+
+def packed_weight_bytes(p):
+    return p.d_out * p.d_in * 18 // 64 + p.d_out * (p.d_in // 128) * 4
+
+
+def kernel_sources_digest():
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "bit_vector_quantized_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(name):
+    """HBM bytes per launch measured with rocprofv3 counters (profiles/), valid only for the
+    kernel sources they were measured on."""
+    path = os.path.join(ROOT, "profiles", f"{name}.traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_sources") != kernel_sources_digest():
+        return None
+    return d.get("traffic_bytes")
+
+
+# ------------------------------------------------------------------------------------------------
+# the decoder-layer step
+# ------------------------------------------------------------------------------------------------
+
+class LayerBench:
+    ORDER = (("qkv", ("q", "k", "v"), "attn_in"), ("o", ("o",), "attn_out"),
+             ("gateup", ("gate", "up"), "mlp_in"), ("down", ("down",), "mlp_mid"))
+    DOMINANT = "gateup"
+
+    def __init__(self, copies, steps):
+        import torch
+        import workloads as W
+        import bit_vector_quantized_amd as sage
+        self.sage = sage
+        self.layer = W.decoder_layer()
+        base = {n: upload_pack(c) for n, c in self.layer.mats.items()}
+        self.bytes_per_layer = sum(packed_weight_bytes(p) for p in base.values())
+        if copies <= 0:
+            need = max(2, math.ceil(2 * MALL_BYTES / self.bytes_per_layer) + 1)
+            divisors = [d for d in range(need, 4 * need) if steps % d == 0]
+            copies = divisors[0] if divisors else need
+        self.copies = [base] + [{n: clone_packed(p) for n, p in base.items()}
+                                for _ in range(copies - 1)]
+        self.xs = {k: torch.from_numpy(v).cuda() for k, v in self.layer.xs.items()}
+        self.ys = {n: torch.empty(p.d_out, dtype=torch.float16, device="cuda")
+                   for n, p in base.items()}
+        self.ws = {}
+        for key, names, _ in self.ORDER:
+            ps = [base[n] for n in names]
+            self.ws[key] = sage.workspace(sage.gemv_multi_workspace_bytes(ps), "cuda")
+        self.dom_bytes = sum(algorithmic_bytes(base[n]) for n in ("gate", "up"))
+        torch.cuda.synchronize()
+
+    def step(self, i, ev=None):
+        mats = self.copies[i % len(self.copies)]
+        for key, names, inp in self.ORDER:
+            ps = [mats[n] for n in names]
+            x = self.xs[inp]
+            if ev is not None and key == self.DOMINANT:
+                ev[0].record()
+            self.sage.gemv_multi(ps, [x] * len(ps), [self.ys[n] for n in names], ws=self.ws[key])
+            if ev is not None and key == self.DOMINANT:
+                ev[1].record()
+
+
+def timed_graph(bench, steps, warmup, eager=False):
+    """Returns (wall seconds for `steps` steps, list of dominant-kernel event durations in ms)."""
+    import torch
+    n = len(bench.copies)
+    for i in range(warmup):
+        bench.step(i)
+    torch.cuda.synchronize()
+    if eager:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            bench.step(i, evs[i])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        return t1 - t0, [a.elapsed_time(b) for a, b in evs]
+    # One graph holds `per` steps over consecutive copies; replayed until `steps` are done.
+    per = n
+    while steps % per:
+        per -= 1
+    reps = steps // per
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(per)]
+
+    def capture(with_events):
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(per):
+                    bench.step(i, evs[i] if with_events else None)
+        torch.cuda.synchronize()
+        return g
+
+    # HIP graphs accept captured event records but cannot time them afterwards, so the graph
+    # carries only kernels; the dominant launch is timed with HIP events right after.
+    g = capture(False)
+    g.replay()  # untimed: first replay uploads the graph
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    durs = dominant_eager(bench, per, evs)
+    return t1 - t0, durs
+
+
+def dominant_eager(bench, count, evs):
+    """Dominant launch alone, enqueued behind a GPU sleep so host launch cost stays hidden."""
+    import torch
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2.4e9 * 0.05))  # about 50 ms of device time
+    for i in range(count):
+        mats = bench.copies[i % len(bench.copies)]
+        ps = [mats["gate"], mats["up"]]
+        x = bench.xs["mlp_in"]
+        evs[i][0].record()
+        bench.sage.gemv_multi(ps, [x, x], [bench.ys["gate"], bench.ys["up"]],
+                              ws=bench.ws["gateup"])
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs[:count]]
+
+
+# ------------------------------------------------------------------------------------------------
+# CPU oracle baseline
+# ------------------------------------------------------------------------------------------------
+
+def cpu_baseline(layer, seconds):
+    """The float64 oracle (decode + matrix-vector product per matrix, exactly as the tests use it)
+    run single-threaded over whole passes of the layer's seven matrices until `seconds` elapse."""
+    from threadpoolctl import threadpool_limits
+    from oracle import decoder
+    names = ["q", "k", "v", "o", "gate", "up", "down"]
+    done_bytes = 0
+    matrices = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(1):
+        while True:
+            for n in names:
+                c = layer.mats[n]
+                decoder.gemv(c, layer.xs[layer.input_of[n]])
+                done_bytes += c.d_out * c.d_in * 18 // 64 + c.d_out * (c.d_in // 128) * 4
+                matrices += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": round(done_bytes / dt / 1e9, 6), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{matrices} matrix products ({matrices // 7} passes over the 7-matrix layer),"
+                      f" float64 NumPy decode + matvec, {dt:.1f} s, 1 thread",
+            "tokens_per_s": round(matrices / 7 / dt, 4)}
+
+
+# ------------------------------------------------------------------------------------------------
+# secondary workloads (one JSON line each, for profiling; not the headline line)
+# ------------------------------------------------------------------------------------------------
+
+def bench_single_products(kind, steps, warmup):
+    import torch
+    import workloads as W
+    import bit_vector_quantized_amd as sage
+    lines = []
+    cases = []
+    if kind in ("sweep", "all"):
+        for K, V in W.SPLITS_FIVE:
+            c, x = W.split_sweep_matrix(K, V)
+            cases.append((f"sweep_9728x2560_K{K}V{V}", c, x, 1))
+    if kind in ("single", "all"):
+        for name, c in W.decoder_layer().mats.items():
+            cases.append((f"layer_{name}_{c.d_out}x{c.d_in}", c, None, 1))
+    if kind in ("gemm", "all"):
+        for shape in ((9728, 2560), (2560, 9728)):
+            for M in (1, 4, 16, 64):
+                c, X = W.small_batch(shape[0], shape[1], M)
+                cases.append((f"gemm_{shape[0]}x{shape[1]}_M{M}", c, X, M))
+    for name, c, x, M in cases:
+        log(f"[case] {name}")
+        base = upload_pack(c)
+        pb = packed_weight_bytes(base)
+        copies = max(2, math.ceil(2 * MALL_BYTES / pb) + 1)
+        ps = [base] + [clone_packed(base) for _ in range(copies - 1)]
+        if M == 1 and (x is None or x.ndim == 1):
+            xd = torch.randn(c.d_in, dtype=torch.float16, device="cuda") if x is None \
+                else torch.from_numpy(x).cuda()
+            y = torch.empty(c.d_out, dtype=torch.float16, device="cuda")
+            ws = sage.workspace(sage.gemv_workspace_bytes(base), "cuda")
+            fn = lambda p: sage.gemv(p, xd, y, ws=ws)
+        else:
+            Xd = torch.from_numpy(x).cuda()
+            Y = torch.empty((M, c.d_out), dtype=torch.float16, device="cuda")
+            ws = sage.workspace(sage.gemm_small_workspace_bytes(base, M), "cuda")
+            fn = lambda p: sage.gemm_small(p, Xd, Y, ws=ws)
+        for i in range(warmup):
+            fn(ps[i % copies])
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(copies):
+                    fn(ps[i])
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, steps // copies)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / (reps * copies)
+        alg = algorithmic_bytes(base, n_x=M) + (M - 1) * c.d_out * 2
+        line = {"workload": name, "us_per_call": round(dt * 1e6, 3),
+                "packed_gbs": round(pb / dt / 1e9, 1), "effective_gbs": round(alg / dt / 1e9, 1),
+                "pct_hbm_peak": round(100 * alg / dt / 1e9 / HBM_PEAK_GBS, 1), "copies": copies}
+        if M > 1:
+            fl = 2.0 * M * c.d_out * c.d_in
+            line["tflops"] = round(fl / dt / 1e12, 2)
+            line["pct_mfma_peak"] = round(100 * fl / dt / 1e12 / MFMA_F16_PEAK_TFLOPS, 2)
+        print(json.dumps(line), flush=True)
+        lines.append(line)
+        del ps, base
+        torch.cuda.empty_cache()
+    return lines
+
+
+def bench_moe(steps, warmup):
+    import numpy as np
+    import torch
+    import workloads as W
+    import bit_vector_quantized_amd as sage
+    log("[case] moe")
+    moe = W.moe_layer(experts_to_build=range(128))
+    packs = [[upload_pack(moe.experts[e][n]) for n in ("gate", "up", "down")] for e in range(128)]
+    all_bytes = sum(packed_weight_bytes(p) for ex in packs for p in ex)
+    copies = max(2, math.ceil(2 * MALL_BYTES / all_bytes) + 1)
+    # every copy's matrices stay referenced here (and by their table) while any launch can run
+    copy_packs = [packs] + [[[clone_packed(p) for p in ex] for ex in packs]
+                            for _ in range(copies - 1)]
+    tables = [sage.expert_table(cp, "cuda")[0] for cp in copy_packs]
+    ids = torch.from_numpy(moe.ids).cuda()
+    x = torch.from_numpy(moe.x).cuda()
+    h = torch.from_numpy(np.ascontiguousarray(moe.h)).cuda()
+    k = len(moe.ids)
+    yg = torch.empty((k, W.MOE_INTER), dtype=torch.float16, device="cuda")
+    yu = torch.empty_like(yg)
+    yd = torch.empty((k, W.MOE_HIDDEN), dtype=torch.float16, device="cuda")
+    shapes = [(W.MOE_INTER, W.MOE_HIDDEN)] * 2 + [(W.MOE_HIDDEN, W.MOE_INTER)]
+    ws = sage.workspace(sage.moe_gemv_workspace_bytes(shapes, k), "cuda")
+    fn = lambda t: sage.moe_gemv(t, 128, shapes, ids, [x, x, h], [0, 0, W.MOE_INTER],
+                                 [yg, yu, yd], [W.MOE_INTER, W.MOE_INTER, W.MOE_HIDDEN], ws=ws)
+    for i in range(warmup):
+        fn(tables[i % copies])
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(copies):
+                fn(tables[i])
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // copies)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / (reps * copies)
+    routed = [packs[int(e)] for e in moe.ids]
+    pb = sum(packed_weight_bytes(p) for ex in routed for p in ex)
+    alg = sum(algorithmic_bytes(p) for ex in routed for p in ex)
+    line = {"workload": "moe_qwen3_30b_a3b_top8_of_128", "us_per_call": round(dt * 1e6, 3),
+            "packed_gbs": round(pb / dt / 1e9, 1), "effective_gbs": round(alg / dt / 1e9, 1),
+            "pct_hbm_peak": round(100 * alg / dt / 1e9 / HBM_PEAK_GBS, 1),
+            "tokens_per_s": round(1.0 / dt, 1), "copies": copies}
+    print(json.dumps(line), flush=True)
+    return line
+
+
+# ------------------------------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the SAGE decode path here runs on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import bit_vector_quantized_amd as sage
+    sage.lib()  # fails loudly when the HIP library is missing
+
+    if args.workload in ("sweep", "gemm", "single", "all"):
+        bench_single_products(args.workload, args.steps, args.warmup)
+    if args.workload in ("moe", "all"):
+        bench_moe(args.steps, args.warmup)
+    if args.workload != "layer":
+        return
+
+    log("[bench] building the decoder layer copies")
+    bench = LayerBench(args.copies, args.steps)
+    log(f"[bench] {len(bench.copies)} copies x {bench.bytes_per_layer} packed bytes; "
+        f"timing {args.steps} steps after {args.warmup} warmup steps")
+    wall, durs = timed_graph(bench, args.steps, args.warmup, eager=args.eager)
+    ms_per_step = wall * 1e3 / args.steps
+    value = bench.bytes_per_layer / (ms_per_step * 1e-3) / 1e9
+    dom_ms = sum(durs) / len(durs) if durs else None
+    roofline = None
+    if dom_ms:
+        achieved = bench.dom_bytes / (dom_ms * 1e-3) / 1e9
+        roofline = {"kernel": "gemv_kernel (gate|up, 2 x 9728x2560 in one launch)",
+                    "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": load_traffic("gemv_gateup_9728x2560x2"),
+                    "avg_launch_us": round(dom_ms * 1e3, 3),
+                    "algorithmic_bytes_per_launch": bench.dom_bytes}
+    line = {
+        "metric": "batch-1 VQ GEMV effective packed-weight GB/s and % of HBM peak; tokens/s",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp16 (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": "qwen3_4b_decoder_layer_batch1", "split_K_V": [64, 4],
+                   "matrices": 7, "launches_per_step": 4,
+                   "packed_bytes_per_step": bench.bytes_per_layer,
+                   "weight_copies": len(bench.copies), "timing": "eager" if args.eager else "hip_graph"},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(1e3 / ms_per_step, 1),
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        line["cpu_baseline"] = cpu_baseline(bench.layer, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -272,14 +272,19 @@ def gemm_small(p: Packed, X, Y=None, ws=None, stream=None):
 
 
 def expert_table(experts: Sequence[Sequence[Packed]], device):
-    """Device array of descriptors, expert e's matrix j at e*n_mats + j (for moe_gemv)."""
+    """Device array of descriptors, expert e's matrix j at e*n_mats + j (for moe_gemv).
+
+    The returned tensor keeps references to the Packed matrices it points at, so their device
+    buffers stay allocated for as long as the table is alive."""
     torch = _torch()
     n_mats = len(experts[0])
     flat = [m for ex in experts for m in ex]
     arr = _mat_array(flat)
     raw = bytes(arr)
     host = torch.frombuffer(bytearray(raw), dtype=torch.uint8)
-    return host.to(device), n_mats
+    table = host.to(device)
+    table._sage_matrices = flat
+    return table, n_mats
 
 
 def moe_gemv_workspace_bytes(shapes: Sequence[tuple], n_sel: int) -> int:

@@ -39,7 +39,7 @@ __global__ void __launch_bounds__(256) dequant_kernel(const uint8_t* __restrict_
     const double ci = (double)h2f(c[i]);
     const double wi = r * (((sbyte >> i) & 1u) ? -ci : ci);
     const int p = sv * 8 + i;
-    const int col = pi ? pi[p] : p;
+    const int col = pi ? (int)min((uint32_t)pi[p], (uint32_t)d_in - 1u) : p;
     wrow[col] = f64_to_f16_rne(wi);
   }
 }

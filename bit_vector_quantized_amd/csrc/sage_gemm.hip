@@ -51,7 +51,7 @@ template <int L, int NT>
 __device__ void gemm_body(const GemmArgs& A, int rt, int split, int mchunk, uint8_t* smem) {
   constexpr uint32_t kK = 1u << L;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int j = lane & 15;      // weight row inside the wave's 16
   const int u = lane >> 4;      // channel quadrant
@@ -68,8 +68,11 @@ __device__ void gemm_body(const GemmArgs& A, int rt, int split, int mchunk, uint
   _Float16* xs = reinterpret_cast<_Float16*>(smem + kK * 256);
   {
     const uint4* cbg = reinterpret_cast<const uint4*>(A.codebook);
-    for (int e = tid; e < (int)kK * 16; e += kGemmThreads)
-      *reinterpret_cast<uint4*>(cb + (e >> 4) * 256 + (e & 15) * 16) = cbg[e >> 4];
+    for (int z = tid; z < (int)kK; z += kGemmThreads) {
+      const uint4 cw = cbg[z];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) *reinterpret_cast<uint4*>(cb + z * 256 + r * 16) = cw;
+    }
     const int cols = ngl * kGroupCols;
     const int c0 = g0 * kGroupCols;
     for (int e = tid; e < NT * 16 * cols; e += kGemmThreads) {
@@ -78,7 +81,7 @@ __device__ void gemm_body(const GemmArgs& A, int rt, int split, int mchunk, uint
       _Float16 v = (_Float16)0.0f;
       if (m < mrows) {
         const int col = c0 + p;
-        const int src = A.pi ? A.pi[col] : col;
+        const int src = A.pi ? (int)min((uint32_t)A.pi[col], (uint32_t)A.d_in - 1u) : col;
         v = __builtin_bit_cast(_Float16, A.X[(int64_t)(m0 + m) * A.ldx + src]);
       }
       xs[m * xstride + p] = v;
@@ -155,28 +158,32 @@ __device__ void gemm_body(const GemmArgs& A, int rt, int split, int mchunk, uint
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = t * 16 + 4 * u + r;
-        if (m < mrows) part[((int64_t)split * A.mrows_chunk + m) * rows_pad + wrow] = acc[t][r];
+        if (m < mrows)
+          store_coherent(part + ((int64_t)split * A.mrows_chunk + m) * rows_pad + wrow, acc[t][r]);
       }
   }
-  __threadfence();
+  wait_stores();
   __syncthreads();
   uint32_t* flag = reinterpret_cast<uint32_t*>(smem);
   uint32_t* counter = A.counters + (int64_t)mchunk * A.rt + rt;
-  if (tid == 0) *flag = (atomicAdd(counter, 1u) == (uint32_t)(A.S - 1)) ? 1u : 0u;
+  if (tid == 0) *flag = (counter_add(counter) == (uint32_t)(A.S - 1)) ? 1u : 0u;
   __syncthreads();
   if (*flag == 0u) return;
-  __threadfence();
   // last workgroup: reduce this row tile for all rows of the chunk
   for (int e = tid; e < mrows * kTileRows; e += kGemmThreads) {
     const int m = e / kTileRows;
     const int row = rt * kTileRows + (e % kTileRows);
     if (row >= A.d_out) continue;
+    const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(
+        part, (uint32_t)((int64_t)A.S * A.mrows_chunk * rows_pad * (int64_t)sizeof(float)));
     float sum = 0.0f;
+#pragma unroll 16
     for (int sp = 0; sp < A.S; ++sp)
-      sum += __builtin_nontemporal_load(part + ((int64_t)sp * A.mrows_chunk + m) * rows_pad + row);
+      sum += load_coherent_at(
+          rs, (uint32_t)((((int64_t)sp * A.mrows_chunk + m) * rows_pad + row) * sizeof(float)));
     A.Y[(int64_t)(m0 + m) * A.ldy + row] = f2h(sum);
   }
-  if (tid == 0) atomicExch(counter, 0u);
+  if (tid == 0) counter_reset(counter);
 }
 
 template <int NT>
@@ -198,6 +205,12 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_kernel(GemmArgs A) {
 
 int tiles_for(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
 
+constexpr size_t kLdsLimit = 160 * 1024;
+
+size_t lds_for(int L, int nt, int gs) {
+  return ((size_t)1 << L) * 256 + (size_t)nt * 16 * ((size_t)gs * kGroupCols + 8) * 2;
+}
+
 void plan(GemmArgs& A, int M) {
   A.rt = ceil_div(A.d_out, kTileRows);
   A.ng = A.d_in / kGroupCols;
@@ -210,6 +223,8 @@ void plan(GemmArgs& A, int M) {
   if (s > A.ng) s = A.ng;
   A.gs = ceil_div(A.ng, (int)s);
   if (A.gs > kMaxGS) A.gs = kMaxGS;
+  // keep the codebook replicas plus the activation tile inside 160 KB of LDS
+  while (A.gs > 1 && lds_for(A.L, tiles_for(M), A.gs) > kLdsLimit) --A.gs;
   A.S = ceil_div(A.ng, A.gs);
 }
 
@@ -235,6 +250,7 @@ int sage_gemm_small_workspace_bytes(const sage_matrix_t* m, int M, size_t* bytes
   GemmArgs A{};
   A.d_out = m->d_out;
   A.d_in = m->d_in;
+  A.L = m->log2K;
   plan(A, M);
   *bytes = workspace_for(A);
   return SAGE_OK;
@@ -269,7 +285,7 @@ int sage_gemm_small(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, u
                                              (size_t)A.mchunks * A.S * A.mrows_chunk * A.rt * kTileRows * 4);
   }
   const int nt = tiles_for(M);
-  const size_t lds = ((size_t)1 << A.L) * 256 + (size_t)nt * 16 * (A.gs * kGroupCols + 8) * 2;
+  const size_t lds = lds_for(A.L, nt, A.gs);
   const unsigned grid = (unsigned)(A.mchunks * A.rt * A.S);
   auto launch = [&](auto kern) {
     static bool attr = false;

@@ -17,8 +17,9 @@
 // mu + q*delta applied once to the 8-term dot product (App. A.1 applies the radius after the dot
 // for the same reason: one multiply instead of eight).
 //
-// Split-K partials go to a caller workspace; the last workgroup of a row-tile group (atomic
-// counter) sums them in split order, writes y in fp16 and resets the counter to zero.
+// Split-K partials go to a caller workspace (coherent stores, no cache-wide fences); the last
+// workgroup of a row-tile group (atomic counter) sums them in split order, writes y in fp16 and
+// resets the counter to zero.
 #include "sage_internal.hpp"
 #include "sage_gemv.hpp"
 
@@ -183,7 +184,7 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int i
                                           int split, uint8_t* smem) {
   using C = SplitC<L>;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: addresses in SGPRs
   const int lane = tid & 63;
   const int g0 = split * J.gs;
   const int ngl = min(J.ng - g0, J.gs);
@@ -202,14 +203,20 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int i
   // 2. LDS set-up: replicated codebook, gathered activations, signed-activation tables.
   uint16_t* xp = reinterpret_cast<uint16_t*>(smem + xp_offset<L>(J.gs));
   {
+    // one load per codeword, then its 16 lane-swizzled replicas
     const uint4* cbg = reinterpret_cast<const uint4*>(R.codebook);
-    for (int e = tid; e < (int)C::kK * 16; e += kGemvThreads)
-      *reinterpret_cast<uint4*>(smem + C::kCbOff + (e >> 4) * 256 + (e & 15) * 16) = cbg[e >> 4];
+    for (int z = tid; z < (int)C::kK; z += kGemvThreads) {
+      const uint4 cw = cbg[z];
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        *reinterpret_cast<uint4*>(smem + C::kCbOff + z * 256 + r * 16) = cw;
+    }
     const uint16_t* x = J.x + (int64_t)inst * J.x_stride;
     const int c0 = g0 * kGroupCols;
+    const uint32_t last = (uint32_t)J.d_in - 1u;  // an out-of-range pi entry is clamped
     for (int p = tid; p < ngl * kGroupCols; p += kGemvThreads) {
       const int col = c0 + p;
-      xp[p] = x[R.pi ? R.pi[col] : col];
+      xp[p] = x[R.pi ? min((uint32_t)R.pi[col], last) : (uint32_t)col];
     }
   }
   __syncthreads();
@@ -249,29 +256,34 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int i
   }
   float* part = J.partial + (int64_t)inst * J.partial_stride;
   const int64_t rows_pad = (int64_t)J.rt * kTileRows;
-  if (row_ok) part[(int64_t)split * rows_pad + row] = acc;
-  __threadfence();
+  if (row_ok) store_coherent(part + (int64_t)split * rows_pad + row, acc);
+  wait_stores();
   __syncthreads();
   uint32_t* flag = reinterpret_cast<uint32_t*>(smem);  // LDS no longer needed
   uint32_t* counter = J.counters + (int64_t)inst * J.counters_stride + wgrow;
-  if (tid == 0) *flag = (atomicAdd(counter, 1u) == (uint32_t)(J.S - 1)) ? 1u : 0u;
+  if (tid == 0) *flag = (counter_add(counter) == (uint32_t)(J.S - 1)) ? 1u : 0u;
   __syncthreads();
   if (*flag == 0u) return;
-  __threadfence();
   if (row_ok) {
+    // all partials of this row issued back to back, summed in split order
+    const __amdgpu_buffer_rsrc_t rs =
+        coherent_rsrc(part, (uint32_t)(J.S * rows_pad * (int64_t)sizeof(float)));
     float s = 0.0f;
-    for (int sp = 0; sp < J.S; ++sp) s += __builtin_nontemporal_load(part + sp * rows_pad + row);
+#pragma unroll 16
+    for (int sp = 0; sp < J.S; ++sp)
+      s += load_coherent_at(rs, (uint32_t)((sp * rows_pad + row) * sizeof(float)));
     y[row] = f2h(s);
   }
-  if (tid == 0) atomicExch(counter, 0u);
+  if (tid == 0) counter_reset(counter);
 }
 
-__global__ void __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
+__global__ void __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
 gemv_kernel(JobTable T) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int wg = blockIdx.x;
   int jid = 0;
-  while (jid + 1 < T.n && wg >= T.jobs[jid + 1].wg_begin) ++jid;
+#pragma unroll
+  for (int i = 1; i < kMaxJobs; ++i) jid += (wg >= T.wg_begin[i]) ? 1 : 0;
   const Job& J = T.jobs[jid];
   int local = wg - J.wg_begin;
   const int inst = local / J.wg_per_inst;
@@ -280,7 +292,8 @@ gemv_kernel(JobTable T) {
   const int split = local - wgrow * J.S;
   Resolved R;
   if (J.table != nullptr) {
-    const sage_matrix_t* M = J.table + (int64_t)J.ids[inst] * J.tstride + J.toff;
+    const uint32_t e = min((uint32_t)J.ids[inst], (uint32_t)J.n_experts - 1u);
+    const sage_matrix_t* M = J.table + (int64_t)e * J.tstride + J.toff;
     R.packed = static_cast<const uint8_t*>(M->packed);
     R.codebook = M->codebook;
     R.pi = M->pi;
@@ -366,10 +379,12 @@ int finish_and_launch(JobTable& T, void* ws, size_t ws_bytes, hipStream_t stream
     }
     need += bytes;
     J.wg_begin = wg;
+    T.wg_begin[i] = wg;
     wg += J.wg_per_inst * J.inst;
     const size_t l = lds_bytes(maxL, J.gs);
     if (l > lds) lds = l;
   }
+  for (int i = T.n; i < kMaxJobs; ++i) T.wg_begin[i] = 0x7FFFFFFF;
   if (need > ws_bytes) return SAGE_ERR_WORKSPACE;
   if (need && !aligned(ws, 256)) return SAGE_ERR_ALIGN;
   T.total_wg = wg;
@@ -524,6 +539,7 @@ int sage_moe_gemv(const sage_matrix_t* experts_dev, int n_experts, const sage_ma
     J = Job{};
     J.table = experts_dev;
     J.ids = ids_dev;
+    J.n_experts = n_experts;
     J.tstride = n_mats;
     J.toff = j;
     plan_job(J, shapes[j].d_out, shapes[j].d_in, gs, n_sel);

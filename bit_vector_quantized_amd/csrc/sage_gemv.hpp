@@ -26,7 +26,7 @@ struct Job {
   int64_t x_stride;        // elements between the inputs of consecutive instances
   int64_t y_stride;        // elements between the outputs of consecutive instances
   int64_t partial_stride;  // floats of split-K partials per instance
-  int32_t tstride, toff;
+  int32_t tstride, toff, n_experts;
   int32_t log2K;
   int32_t d_out, d_in;
   int32_t rt, ng, wgr;     // row tiles, column groups, workgroup rows (= ceil(rt / 4))
@@ -36,6 +36,7 @@ struct Job {
 };
 
 struct JobTable {
+  int32_t wg_begin[kMaxJobs];  // first workgroup of each job (unused entries: INT32_MAX)
   int32_t n;
   int32_t total_wg;
   Job jobs[kMaxJobs];

@@ -91,6 +91,31 @@ int check_matrix(const sage_matrix_t* m);   // shape, split, pointers, alignment
 int hip_status();                            // SAGE_ERR_HIP if the last launch failed
 int device_cu_count();                       // compute units of the current device (cached)
 
+// Cross-workgroup hand-off of split-K partials without cache-wide fences. Partials are written with
+// agent-scope relaxed atomic stores (coherent stores, sc1) and read back the same way; each wave
+// waits for its stores to be acknowledged before the workgroup barrier that precedes the counter
+// increment, so a workgroup that sees the final count also sees every partial.
+__device__ inline void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Coherent (sc1) loads through a buffer descriptor: unlike atomic loads they can be batched.
+__device__ inline __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ inline float load_coherent_at(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0x10 /* sc1 */));
+}
+__device__ inline uint32_t counter_add(uint32_t* c) {
+  return __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void counter_reset(uint32_t* c) {
+  __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // fp16 <-> fp32 on bit patterns; the float -> half conversion rounds to nearest even.
 __device__ inline float h2f(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits16 & 0xFFFFu));
