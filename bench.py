@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--eager", action="store_true", help="launch from Python (no graph)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 256 MiB device copy (a kernel of known traffic, used to "
+                         "scale rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     return ap.parse_args()
 
 
@@ -400,6 +403,14 @@ def main():
     if args.workload != "layer":
         return
 
+    if args.copy_calibration:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] calibration copy: 268435456 bytes read, 268435456 bytes written")
+        del src, dst
     log("[bench] building the decoder layer copies")
     bench = LayerBench(args.copies, args.steps)
     log(f"[bench] {len(bench.copies)} copies x {bench.bytes_per_layer} packed bytes; "

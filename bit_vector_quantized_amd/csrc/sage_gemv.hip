@@ -179,16 +179,17 @@ __device__ __forceinline__ float group_dot(const GroupRegs& R, uint32_t laneoff,
   return acc;
 }
 
-template <int L>
+template <int L, int W>
 __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int inst, int wgrow,
                                           int split, uint8_t* smem) {
+  constexpr int kThreads = W * 64;
   using C = SplitC<L>;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: addresses in SGPRs
   const int lane = tid & 63;
   const int g0 = split * J.gs;
   const int ngl = min(J.ng - g0, J.gs);
-  const int rt = wgrow * kGemvWaves + wave;
+  const int rt = wgrow * W + wave;
   const bool tile_ok = rt < J.rt;
 
   // 1. Issue this wave's packed loads for its first two groups before the LDS set-up; later
@@ -205,7 +206,7 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int i
   {
     // one load per codeword, then its 16 lane-swizzled replicas
     const uint4* cbg = reinterpret_cast<const uint4*>(R.codebook);
-    for (int z = tid; z < (int)C::kK; z += kGemvThreads) {
+    for (int z = tid; z < (int)C::kK; z += kThreads) {
       const uint4 cw = cbg[z];
 #pragma unroll
       for (int r = 0; r < 16; ++r)
@@ -214,13 +215,13 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int i
     const uint16_t* x = J.x + (int64_t)inst * J.x_stride;
     const int c0 = g0 * kGroupCols;
     const uint32_t last = (uint32_t)J.d_in - 1u;  // an out-of-range pi entry is clamped
-    for (int p = tid; p < ngl * kGroupCols; p += kGemvThreads) {
+    for (int p = tid; p < ngl * kGroupCols; p += kThreads) {
       const int col = c0 + p;
       xp[p] = x[R.pi ? min((uint32_t)R.pi[col], last) : (uint32_t)col];
     }
   }
   __syncthreads();
-  for (int e = tid; e < ngl * kSubPerGroup * 16; e += kGemvThreads) {
+  for (int e = tid; e < ngl * kSubPerGroup * 16; e += kThreads) {
     const int step = e >> 4;
     const uint32_t n = (uint32_t)(e & 15);
     const uint4 v = *reinterpret_cast<const uint4*>(xp + step * 8);
@@ -277,7 +278,8 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int i
   if (tid == 0) counter_reset(counter);
 }
 
-__global__ void __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
+template <int W>
+__global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(3, 8)))
 gemv_kernel(JobTable T) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int wg = blockIdx.x;
@@ -305,11 +307,11 @@ gemv_kernel(JobTable T) {
     R.L = J.log2K;
   }
   switch (R.L) {
-    case 4: gemv_body<4>(R, J, inst, wgrow, split, smem); break;
-    case 5: gemv_body<5>(R, J, inst, wgrow, split, smem); break;
-    case 6: gemv_body<6>(R, J, inst, wgrow, split, smem); break;
-    case 7: gemv_body<7>(R, J, inst, wgrow, split, smem); break;
-    default: gemv_body<8>(R, J, inst, wgrow, split, smem); break;
+    case 4: gemv_body<4, W>(R, J, inst, wgrow, split, smem); break;
+    case 5: gemv_body<5, W>(R, J, inst, wgrow, split, smem); break;
+    case 6: gemv_body<6, W>(R, J, inst, wgrow, split, smem); break;
+    case 7: gemv_body<7, W>(R, J, inst, wgrow, split, smem); break;
+    default: gemv_body<8, W>(R, J, inst, wgrow, split, smem); break;
   }
 }
 
@@ -330,23 +332,32 @@ size_t lds_bytes(int maxL, int gs) {
   return need;
 }
 
-int plan_groups_per_split(int64_t total_blocks) {
-  // About 2.5 workgroups of 4 row tiles per compute unit; more groups per split when the work is
-  // large enough, so the LDS set-up is amortised over more blocks.
-  const int64_t target_wg = (int64_t)device_cu_count() * 5 / 2;
-  int64_t gs = total_blocks / (kGemvWaves * target_wg);
-  if (gs < 1) gs = 1;
-  if (gs > kMaxGroupsPerSplit) gs = kMaxGroupsPerSplit;
-  return (int)gs;
+// Launch plan shared by every job of one launch: wavefronts per workgroup and groups per split.
+struct LaunchPlan {
+  int waves;
+  int gs;
+};
+
+LaunchPlan plan_launch(int64_t total_blocks, int64_t total_row_tiles) {
+  // Four row tiles per workgroup, so three workgroups fit a compute unit at once and every launch
+  // runs in a single round; groups per split grow until the launch would drop below one
+  // workgroup per compute unit (more groups per split = fewer split-K partials to combine).
+  (void)total_row_tiles;
+  const int64_t target = (int64_t)device_cu_count();
+  for (int gs = kMaxGroupsPerSplit; gs > 1; --gs) {
+    const int64_t wgs = (total_blocks + 4 * gs - 1) / (4 * gs);
+    if (wgs >= target) return LaunchPlan{4, gs};
+  }
+  return LaunchPlan{4, 1};
 }
 
-void plan_job(Job& J, int d_out, int d_in, int gs_hint, int instances) {
+void plan_job(Job& J, int d_out, int d_in, const LaunchPlan& P, int instances) {
   J.d_out = d_out;
   J.d_in = d_in;
   J.rt = ceil_div(d_out, kTileRows);
   J.ng = d_in / kGroupCols;
-  J.wgr = ceil_div(J.rt, kGemvWaves);
-  J.gs = gs_hint < J.ng ? gs_hint : J.ng;
+  J.wgr = ceil_div(J.rt, P.waves);
+  J.gs = P.gs < J.ng ? P.gs : J.ng;
   J.S = ceil_div(J.ng, J.gs);
   J.gs = ceil_div(J.ng, J.S);
   J.wg_per_inst = J.wgr * J.S;
@@ -391,12 +402,17 @@ int finish_and_launch(JobTable& T, void* ws, size_t ws_bytes, hipStream_t stream
   if (wg == 0) return SAGE_OK;
   static bool attr_done = false;
   if (!attr_done) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_kernel),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_kernel<4>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess ||
+        hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_kernel<8>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
       return SAGE_ERR_HIP;
     attr_done = true;
   }
-  hipLaunchKernelGGL(gemv_kernel, dim3(wg), dim3(kGemvThreads), lds, stream, T);
+  if (T.waves == 8)
+    hipLaunchKernelGGL(gemv_kernel<8>, dim3(wg), dim3(8 * 64), lds, stream, T);
+  else
+    hipLaunchKernelGGL(gemv_kernel<4>, dim3(wg), dim3(4 * 64), lds, stream, T);
   return hip_status();
 }
 
@@ -412,20 +428,23 @@ using namespace sage;
 
 namespace {
 
-void direct_job(Job& J, const sage_matrix_t* m, int gs) {
+void direct_job(Job& J, const sage_matrix_t* m, const LaunchPlan& P) {
   J = Job{};
   J.packed = static_cast<const uint8_t*>(m->packed);
   J.codebook = m->codebook;
   J.pi = m->pi;
   J.log2K = m->log2K;
-  plan_job(J, m->d_out, m->d_in, gs, 1);
+  plan_job(J, m->d_out, m->d_in, P, 1);
 }
 
-int gs_for(const sage_matrix_t* mats, int n) {
-  int64_t blocks = 0;
-  for (int i = 0; i < n; ++i)
-    blocks += (int64_t)ceil_div(mats[i].d_out, kTileRows) * (mats[i].d_in / kGroupCols);
-  return plan_groups_per_split(blocks);
+LaunchPlan plan_for(const sage_matrix_t* mats, int n, int instances = 1) {
+  int64_t blocks = 0, tiles = 0;
+  for (int i = 0; i < n; ++i) {
+    const int64_t rt = ceil_div(mats[i].d_out, kTileRows);
+    blocks += (int64_t)instances * rt * (mats[i].d_in / kGroupCols);
+    tiles += (int64_t)instances * rt;
+  }
+  return plan_launch(blocks, tiles);
 }
 
 }  // namespace
@@ -437,7 +456,7 @@ int sage_gemv_workspace_bytes(const sage_matrix_t* m, size_t* bytes) {
   int st = check_matrix(m);
   if (st != SAGE_OK) return st;
   Job J;
-  direct_job(J, m, gs_for(m, 1));
+  direct_job(J, m, plan_for(m, 1));
   *bytes = job_workspace_bytes(J);
   return SAGE_OK;
 }
@@ -456,11 +475,11 @@ int sage_gemv_multi_workspace_bytes(const sage_matrix_t* mats, int n, size_t* by
     int st = check_matrix(&mats[i]);
     if (st != SAGE_OK) return st;
   }
-  const int gs = gs_for(mats, n);
+  const LaunchPlan P = plan_for(mats, n);
   size_t need = 0;
   for (int i = 0; i < n; ++i) {
     Job J;
-    direct_job(J, &mats[i], gs);
+    direct_job(J, &mats[i], P);
     need += job_workspace_bytes(J);
   }
   *bytes = need;
@@ -479,10 +498,11 @@ int sage_gemv_multi(const sage_matrix_t* mats, const uint16_t* const* xs, uint16
   }
   JobTable T{};
   T.n = n;
-  const int gs = gs_for(mats, n);
+  const LaunchPlan P = plan_for(mats, n);
+  T.waves = P.waves;
   int maxL = 4;
   for (int i = 0; i < n; ++i) {
-    direct_job(T.jobs[i], &mats[i], gs);
+    direct_job(T.jobs[i], &mats[i], P);
     T.jobs[i].x = xs[i];
     T.jobs[i].y = ys[i];
     if (mats[i].log2K > maxL) maxL = mats[i].log2K;
@@ -494,17 +514,15 @@ int sage_moe_gemv_workspace_bytes(const sage_matrix_t* shapes, int n_mats, int n
                                   size_t* bytes) {
   if (bytes == nullptr || shapes == nullptr) return SAGE_ERR_NULL;
   if (n_mats < 1 || n_mats > kMaxJobs || n_sel < 1) return SAGE_ERR_ARG;
-  int64_t blocks = 0;
   for (int j = 0; j < n_mats; ++j) {
     int st = check_shape(shapes[j].d_out, shapes[j].d_in);
     if (st != SAGE_OK) return st;
-    blocks += (int64_t)n_sel * ceil_div(shapes[j].d_out, kTileRows) * (shapes[j].d_in / kGroupCols);
   }
-  const int gs = plan_groups_per_split(blocks);
+  const LaunchPlan P = plan_for(shapes, n_mats, n_sel);
   size_t need = 0;
   for (int j = 0; j < n_mats; ++j) {
     Job J{};
-    plan_job(J, shapes[j].d_out, shapes[j].d_in, gs, n_sel);
+    plan_job(J, shapes[j].d_out, shapes[j].d_in, P, n_sel);
     need += job_workspace_bytes(J);
   }
   *bytes = need;
@@ -521,7 +539,6 @@ int sage_moe_gemv(const sage_matrix_t* experts_dev, int n_experts, const sage_ma
   if (n_experts < 1 || n_mats < 1 || n_mats > kMaxJobs || n_sel < 1 || n_sel > n_experts)
     return SAGE_ERR_ARG;
   if (!aligned(experts_dev, 8) || !aligned(ids_dev, 4)) return SAGE_ERR_ALIGN;
-  int64_t blocks = 0;
   for (int j = 0; j < n_mats; ++j) {
     int st = check_shape(shapes[j].d_out, shapes[j].d_in);
     if (st != SAGE_OK) return st;
@@ -529,11 +546,11 @@ int sage_moe_gemv(const sage_matrix_t* experts_dev, int n_experts, const sage_ma
     if (!aligned(xs[j], 4) || !aligned(ys[j], 2)) return SAGE_ERR_ALIGN;
     if (x_strides[j] < 0 || (x_strides[j] & 1) || y_strides[j] < 0) return SAGE_ERR_ARG;
     if (n_sel > 1 && y_strides[j] < shapes[j].d_out) return SAGE_ERR_ARG;
-    blocks += (int64_t)n_sel * ceil_div(shapes[j].d_out, kTileRows) * (shapes[j].d_in / kGroupCols);
   }
-  const int gs = plan_groups_per_split(blocks);
+  const LaunchPlan P = plan_for(shapes, n_mats, n_sel);
   JobTable T{};
   T.n = n_mats;
+  T.waves = P.waves;
   for (int j = 0; j < n_mats; ++j) {
     Job& J = T.jobs[j];
     J = Job{};
@@ -542,7 +559,7 @@ int sage_moe_gemv(const sage_matrix_t* experts_dev, int n_experts, const sage_ma
     J.n_experts = n_experts;
     J.tstride = n_mats;
     J.toff = j;
-    plan_job(J, shapes[j].d_out, shapes[j].d_in, gs, n_sel);
+    plan_job(J, shapes[j].d_out, shapes[j].d_in, P, n_sel);
     J.x = xs[j];
     J.x_stride = x_strides[j];
     J.y = ys[j];

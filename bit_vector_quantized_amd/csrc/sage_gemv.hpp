@@ -5,8 +5,7 @@
 
 namespace sage {
 
-constexpr int kGemvWaves = 4;                 // row tiles per workgroup
-constexpr int kGemvThreads = kGemvWaves * 64;
+constexpr int kMaxWaves = 8;                  // row tiles per workgroup: 4 or 8 per launch
 constexpr int kMaxGroupsPerSplit = 8;         // column groups one workgroup handles
 constexpr int kMaxJobs = 16;
 
@@ -29,7 +28,7 @@ struct Job {
   int32_t tstride, toff, n_experts;
   int32_t log2K;
   int32_t d_out, d_in;
-  int32_t rt, ng, wgr;     // row tiles, column groups, workgroup rows (= ceil(rt / 4))
+  int32_t rt, ng, wgr;     // row tiles, column groups, workgroup rows (= ceil(rt / waves))
   int32_t S, gs;           // column splits and groups per split
   int32_t wg_begin, wg_per_inst, inst;
   int32_t counters_stride;
@@ -37,6 +36,7 @@ struct Job {
 
 struct JobTable {
   int32_t wg_begin[kMaxJobs];  // first workgroup of each job (unused entries: INT32_MAX)
+  int32_t waves;               // row tiles (wavefronts) per workgroup
   int32_t n;
   int32_t total_wg;
   Job jobs[kMaxJobs];
