@@ -35,11 +35,29 @@ struct GemmArgs {
   int32_t d_out, d_in, M, L;
   int32_t rt, ng, S, gs, mchunks;
   int32_t mrows_chunk;  // activation rows per workgroup = 16 * tiles
+  int32_t vec_x;        // X rows are 16-byte aligned and already in permuted order
 };
 
-__device__ inline uint32_t sign_mask_pair(uint32_t s, int i) {
-  // bit i -> sign of the low half, bit i+1 -> sign of the high half
-  return (((s >> i) & 1u) << 15) | (((s >> (i + 1)) & 1u) << 31);
+constexpr int kPermuteMinRows = 8;  // from this many rows on, X is permuted once per call
+
+// Sign masks of one nibble: bits 0/1 -> signs of the first fp16 pair, bits 2/3 -> second pair.
+__device__ inline uint2 nibble_masks(uint32_t n) {
+  return make_uint2(((n & 1u) << 15) | ((n & 2u) << 30), ((n & 4u) << 13) | ((n & 8u) << 28));
+}
+
+// X[:, pi] for M rows into a dense [M][d_in] buffer (the reorder the paper does once per
+// projection before prefill, §3.5).
+__global__ void __launch_bounds__(256) permute_rows_kernel(const uint16_t* __restrict__ X,
+                                                           int64_t ldx,
+                                                           const int32_t* __restrict__ pi,
+                                                           int d_in, int M,
+                                                           uint16_t* __restrict__ Xp) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (int64_t)M * d_in) return;
+  const int m = (int)(t / d_in);
+  const int p = (int)(t - (int64_t)m * d_in);
+  const int src = pi ? (int)min((uint32_t)pi[p], (uint32_t)d_in - 1u) : p;
+  Xp[t] = X[(int64_t)m * ldx + src];
 }
 
 __device__ inline uint32_t mul_pair(uint32_t c, half2_t r) {
@@ -62,10 +80,12 @@ __device__ void gemm_body(const GemmArgs& A, int rt, int split, int mchunk, uint
   const int wrow_in_tile = wave * 16 + j;
   const int wrow = rt * kTileRows + wrow_in_tile;
 
-  // LDS: codebook replicas [K][16][16 B] then X tile [NT*16][ngl*128 (+8 pad)] fp16.
+  // LDS: codebook replicas [K][16][16 B], sign-mask table [16][8 B], then the X tile
+  // [NT*16][gs*128 (+8 pad)] fp16.
   uint8_t* cb = smem;
+  uint2* smask = reinterpret_cast<uint2*>(smem + kK * 256);
   const int xstride = A.gs * kGroupCols + 8;  // fp16 elements per activation row (padded)
-  _Float16* xs = reinterpret_cast<_Float16*>(smem + kK * 256);
+  _Float16* xs = reinterpret_cast<_Float16*>(smem + kK * 256 + 128);
   {
     const uint4* cbg = reinterpret_cast<const uint4*>(A.codebook);
     for (int z = tid; z < (int)kK; z += kGemmThreads) {
@@ -73,18 +93,43 @@ __device__ void gemm_body(const GemmArgs& A, int rt, int split, int mchunk, uint
 #pragma unroll
       for (int r = 0; r < 16; ++r) *reinterpret_cast<uint4*>(cb + z * 256 + r * 16) = cw;
     }
+    if (tid < 16) smask[tid] = nibble_masks((uint32_t)tid);
     const int cols = ngl * kGroupCols;
     const int c0 = g0 * kGroupCols;
-    for (int e = tid; e < NT * 16 * cols; e += kGemmThreads) {
-      const int m = e / cols;
-      const int p = e - m * cols;
-      _Float16 v = (_Float16)0.0f;
-      if (m < mrows) {
-        const int col = c0 + p;
-        const int src = A.pi ? (int)min((uint32_t)A.pi[col], (uint32_t)A.d_in - 1u) : col;
-        v = __builtin_bit_cast(_Float16, A.X[(int64_t)(m0 + m) * A.ldx + src]);
+    if (A.vec_x) {
+      // 16-byte chunks of already-permuted rows, eight loads in flight per thread
+      const int chunks = cols / 8;
+      const int total = NT * 16 * chunks;
+      for (int base = 0; base < total; base += 8 * kGemmThreads) {
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int e = base + u * kGemmThreads + tid;
+          const int m = e / chunks;
+          v[u] = make_uint4(0, 0, 0, 0);
+          if (e < total && m < mrows)
+            v[u] = *reinterpret_cast<const uint4*>(A.X + (int64_t)(m0 + m) * A.ldx + c0 +
+                                                   (e - m * chunks) * 8);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int e = base + u * kGemmThreads + tid;
+          const int m = e / chunks;
+          if (e < total) *reinterpret_cast<uint4*>(xs + m * xstride + (e - m * chunks) * 8) = v[u];
+        }
       }
-      xs[m * xstride + p] = v;
+    } else {
+      for (int e = tid; e < NT * 16 * cols; e += kGemmThreads) {
+        const int m = e / cols;
+        const int p = e - m * cols;
+        _Float16 v = (_Float16)0.0f;
+        if (m < mrows) {
+          const int col = c0 + p;
+          const int src = A.pi ? (int)min((uint32_t)A.pi[col], (uint32_t)A.d_in - 1u) : col;
+          v = __builtin_bit_cast(_Float16, A.X[(int64_t)(m0 + m) * A.ldx + src]);
+        }
+        xs[m * xstride + p] = v;
+      }
     }
   }
   __syncthreads();
@@ -120,11 +165,13 @@ __device__ void gemm_body(const GemmArgs& A, int rt, int split, int mchunk, uint
       const _Float16 rh = (_Float16)r;
       const half2_t r2 = half2_t{rh, rh};
       const uint4 c = *reinterpret_cast<const uint4*>(cb + z * 256 + laneoff);
+      const uint2 mlo = smask[s & 15u];
+      const uint2 mhi = smask[s >> 4];
       uint32_t w[4];
-      w[0] = mul_pair(c.x ^ sign_mask_pair(s, 0), r2);
-      w[1] = mul_pair(c.y ^ sign_mask_pair(s, 2), r2);
-      w[2] = mul_pair(c.z ^ sign_mask_pair(s, 4), r2);
-      w[3] = mul_pair(c.w ^ sign_mask_pair(s, 6), r2);
+      w[0] = mul_pair(c.x ^ mlo.x, r2);
+      w[1] = mul_pair(c.y ^ mlo.y, r2);
+      w[2] = mul_pair(c.z ^ mhi.x, r2);
+      w[3] = mul_pair(c.w ^ mhi.y, r2);
       if (!row_ok) w[0] = w[1] = w[2] = w[3] = 0u;
       const half8_t b = __builtin_bit_cast(half8_t, make_uint4(w[0], w[1], w[2], w[3]));
       const int xcol = k * kGroupCols + (4 * u + kk) * 8;
@@ -169,19 +216,39 @@ __device__ void gemm_body(const GemmArgs& A, int rt, int split, int mchunk, uint
   if (tid == 0) *flag = (counter_add(counter) == (uint32_t)(A.S - 1)) ? 1u : 0u;
   __syncthreads();
   if (*flag == 0u) return;
-  // last workgroup: reduce this row tile for all rows of the chunk
-  for (int e = tid; e < mrows * kTileRows; e += kGemmThreads) {
-    const int m = e / kTileRows;
-    const int row = rt * kTileRows + (e % kTileRows);
-    if (row >= A.d_out) continue;
-    const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(
-        part, (uint32_t)((int64_t)A.S * A.mrows_chunk * rows_pad * (int64_t)sizeof(float)));
-    float sum = 0.0f;
-#pragma unroll 16
-    for (int sp = 0; sp < A.S; ++sp)
-      sum += load_coherent_at(
-          rs, (uint32_t)((((int64_t)sp * A.mrows_chunk + m) * rows_pad + row) * sizeof(float)));
-    A.Y[(int64_t)(m0 + m) * A.ldy + row] = f2h(sum);
+  // last workgroup: reduce this row tile for all rows of the chunk. Thread t owns elements
+  // t + 256 i (activation row 4 i + t / 64, tile row t % 64); the partials of four splits are in
+  // flight at a time and summed in split order.
+  constexpr int kPer = NT * 16 * kTileRows / kGemmThreads;
+  const int trow = rt * kTileRows + (tid & 63);
+  const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(
+      part, (uint32_t)((int64_t)A.S * A.mrows_chunk * rows_pad * (int64_t)sizeof(float)));
+  float sum[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) sum[i] = 0.0f;
+  for (int sp0 = 0; sp0 < A.S; sp0 += 4) {
+    float v[4][kPer];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int m = 4 * i + (tid >> 6);
+        const int sp = min(sp0 + q, A.S - 1);
+        v[q][i] = load_coherent_at(
+            rs, (uint32_t)((((int64_t)sp * A.mrows_chunk + m) * rows_pad + trow) * sizeof(float)));
+      }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (sp0 + q < A.S) sum[i] += v[q][i];
+  }
+  if (trow < A.d_out) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int m = 4 * i + (tid >> 6);
+      if (m < mrows) A.Y[(int64_t)(m0 + m) * A.ldy + trow] = f2h(sum[i]);
+    }
   }
   if (tid == 0) counter_reset(counter);
 }
@@ -208,7 +275,7 @@ int tiles_for(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
 constexpr size_t kLdsLimit = 160 * 1024;
 
 size_t lds_for(int L, int nt, int gs) {
-  return ((size_t)1 << L) * 256 + (size_t)nt * 16 * ((size_t)gs * kGroupCols + 8) * 2;
+  return ((size_t)1 << L) * 256 + 128 + (size_t)nt * 16 * ((size_t)gs * kGroupCols + 8) * 2;
 }
 
 void plan(GemmArgs& A, int M) {
@@ -223,16 +290,21 @@ void plan(GemmArgs& A, int M) {
   if (s > A.ng) s = A.ng;
   A.gs = ceil_div(A.ng, (int)s);
   if (A.gs > kMaxGS) A.gs = kMaxGS;
-  // keep the codebook replicas plus the activation tile inside 160 KB of LDS
-  while (A.gs > 1 && lds_for(A.L, tiles_for(M), A.gs) > kLdsLimit) --A.gs;
+  // keep the codebook replicas plus the activation tile small enough for two workgroups per CU
+  while (A.gs > 1 && lds_for(A.L, tiles_for(M), A.gs) > kLdsLimit / 2) --A.gs;
   A.S = ceil_div(A.ng, A.gs);
 }
 
+size_t permuted_bytes(int M, int d_in) {
+  return M >= kPermuteMinRows ? ((size_t)M * d_in * 2 + 255) / 256 * 256 : 0;
+}
+
 size_t workspace_for(const GemmArgs& A) {
-  if (A.S == 1) return 0;
+  const size_t xp = permuted_bytes(A.M, A.d_in);
+  if (A.S == 1) return xp;
   const size_t part = (size_t)A.mchunks * A.S * A.mrows_chunk * A.rt * kTileRows * 4;
   const size_t cnt = (size_t)A.mchunks * A.rt * 4;
-  return (part + cnt + 255) / 256 * 256;
+  return xp + (part + cnt + 255) / 256 * 256;
 }
 
 }  // namespace
@@ -247,9 +319,11 @@ int sage_gemm_small_workspace_bytes(const sage_matrix_t* m, int M, size_t* bytes
   int st = check_matrix(m);
   if (st != SAGE_OK) return st;
   if (M < 1) return SAGE_ERR_SHAPE;
+  if (M == 1) return sage_gemv_workspace_bytes(m, bytes);  // one row: the batch-one kernel
   GemmArgs A{};
   A.d_out = m->d_out;
   A.d_in = m->d_in;
+  A.M = M;
   A.L = m->log2K;
   plan(A, M);
   *bytes = workspace_for(A);
@@ -263,6 +337,7 @@ int sage_gemm_small(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, u
   if (X == nullptr || Y == nullptr) return SAGE_ERR_NULL;
   if (M < 1 || ldx < m->d_in || ldy < m->d_out) return SAGE_ERR_SHAPE;
   if (!aligned(X, 4) || !aligned(Y, 2) || (ldx & 1)) return SAGE_ERR_ALIGN;
+  if (M == 1) return sage_gemv(m, X, Y, ws, ws_bytes, stream);
   GemmArgs A{};
   A.packed = static_cast<const uint8_t*>(m->packed);
   A.codebook = m->codebook;
@@ -277,12 +352,30 @@ int sage_gemm_small(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, u
   A.L = m->log2K;
   plan(A, M);
   const size_t need = workspace_for(A);
+  const size_t xp_bytes = permuted_bytes(M, A.d_in);
   if (need) {
     if (ws == nullptr || ws_bytes < need) return SAGE_ERR_WORKSPACE;
     if (!aligned(ws, 256)) return SAGE_ERR_ALIGN;
-    A.partial = static_cast<float*>(ws);
-    A.counters = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) +
-                                             (size_t)A.mchunks * A.S * A.mrows_chunk * A.rt * kTileRows * 4);
+  }
+  char* wsb = static_cast<char*>(ws);
+  if (A.S > 1) {
+    A.partial = reinterpret_cast<float*>(wsb + xp_bytes);
+    A.counters = reinterpret_cast<uint32_t*>(
+        wsb + xp_bytes + (size_t)A.mchunks * A.S * A.mrows_chunk * A.rt * kTileRows * 4);
+  }
+  hipStream_t hs = (hipStream_t)stream;
+  if (xp_bytes) {
+    // reorder the activations once, then every workgroup reads contiguous 16-byte chunks
+    uint16_t* Xp = reinterpret_cast<uint16_t*>(wsb);
+    const int64_t n = (int64_t)M * A.d_in;
+    hipLaunchKernelGGL(permute_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, hs,
+                       X, (int64_t)ldx, m->pi, A.d_in, M, Xp);
+    A.X = Xp;
+    A.ldx = A.d_in;
+    A.pi = nullptr;
+    A.vec_x = 1;
+  } else {
+    A.vec_x = (A.pi == nullptr && aligned(X, 16) && (ldx % 8) == 0) ? 1 : 0;
   }
   const int nt = tiles_for(M);
   const size_t lds = lds_for(A.L, nt, A.gs);
@@ -291,10 +384,10 @@ int sage_gemm_small(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, u
     static bool attr = false;
     if (!attr) {
       (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
       attr = true;
     }
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kGemmThreads), lds, (hipStream_t)stream, A);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kGemmThreads), lds, hs, A);
   };
   if (nt == 1) launch(gemm_kernel<1>);
   else if (nt == 2) launch(gemm_kernel<2>);

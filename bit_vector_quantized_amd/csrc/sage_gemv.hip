@@ -30,14 +30,11 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-__device__ inline uint4 ld_stream16(const uint8_t* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
+// Range-checked buffer view: loads at offsets past `bytes` return zeros without a memory access.
+__device__ inline __amdgpu_buffer_rsrc_t view(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
-__device__ inline uint2 ld_stream8(const uint8_t* p) {
-  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
-  return make_uint2(v.x, v.y);
-}
+constexpr int kNonTemporal = 2;  // streamed once: no reuse expected in the caches
 
 // First step of a dot chain, accumulator 0 (VOP3P form, so no register needs zeroing first).
 __device__ inline float dot2_z(uint32_t a, uint32_t b) {
@@ -105,14 +102,16 @@ struct GroupRegs {
   uint32_t x, g;
 };
 
-__device__ inline void load_group(GroupRegs& r, const uint8_t* blk, int lane) {
-  const uint4 a = ld_stream16(blk + kPlaneA + lane * 16);
-  const uint4 b = ld_stream16(blk + kPlaneB + lane * 16);
-  const uint2 s = ld_stream8(blk + kSidePlane + lane * 8);
-  r.p[0] = a.x; r.p[1] = a.y; r.p[2] = a.z; r.p[3] = a.w;
-  r.p[4] = b.x; r.p[5] = b.y; r.p[6] = b.z; r.p[7] = b.w;
-  r.x = s.x;
-  r.g = s.y;
+// One group of one lane: main words of subvectors 0-7 and 8-15, then aux fields and the grid.
+__device__ inline void load_group(GroupRegs& r, __amdgpu_buffer_rsrc_t rs, uint32_t blk_off,
+                                  int lane) {
+  const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, blk_off + kPlaneA + lane * 16, 0, kNonTemporal);
+  const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rs, blk_off + kPlaneB + lane * 16, 0, kNonTemporal);
+  const u32x2 s = __builtin_amdgcn_raw_buffer_load_b64(rs, blk_off + kSidePlane + lane * 8, 0, kNonTemporal);
+  r.p[0] = a[0]; r.p[1] = a[1]; r.p[2] = a[2]; r.p[3] = a[3];
+  r.p[4] = b[0]; r.p[5] = b[1]; r.p[6] = b[2]; r.p[7] = b[3];
+  r.x = s[0];
+  r.g = s[1];
 }
 
 // LDS reads at absolute LDS byte addresses. The kernel declares no static LDS, so its dynamic LDS
@@ -179,7 +178,7 @@ __device__ __forceinline__ float group_dot(const GroupRegs& R, uint32_t laneoff,
   return acc;
 }
 
-template <int L, int W>
+template <int L, int W, bool kWholeX>
 __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int inst, int wgrow,
                                           int split, uint8_t* smem) {
   constexpr int kThreads = W * 64;
@@ -192,35 +191,89 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int i
   const int rt = wgrow * W + wave;
   const bool tile_ok = rt < J.rt;
 
-  // 1. Issue this wave's packed loads for its first two groups before the LDS set-up; later
-  //    groups stream through a three-deep register ring (two groups in flight while one computes).
-  GroupRegs ring[3];
+  // 1. Loads, in the order their data is needed. Every load is unconditional: a range-checked
+  //    view returns zeros past the split's last group (or for a wave past the last row tile), so
+  //    the wait before each use covers exactly the loads issued before it.
+  constexpr int kColsPerThread = kMaxGroupsPerSplit * kGroupCols / kThreads;
+  const int c0 = g0 * kGroupCols;
+  const int cols = ngl * kGroupCols;
+  const __amdgpu_buffer_rsrc_t cb_rs = view(R.codebook, C::kK * 16u);
+  const __amdgpu_buffer_rsrc_t pi_rs = view(R.pi ? R.pi + c0 : nullptr, R.pi ? cols * 4u : 0u);
+  const __amdgpu_buffer_rsrc_t x_rs =
+      view(J.x + (int64_t)inst * J.x_stride, (uint32_t)J.d_in * 2u);
   const uint8_t* blk0 = R.packed + ((int64_t)rt * J.ng + g0) * kBlockBytes;
-  if (tile_ok) {
-    if (ngl > 0) load_group(ring[0], blk0, lane);
-    if (ngl > 1) load_group(ring[1], blk0 + kBlockBytes, lane);
-  }
+  const __amdgpu_buffer_rsrc_t w_rs = view(blk0, tile_ok ? (uint32_t)(ngl * kBlockBytes) : 0u);
 
-  // 2. LDS set-up: replicated codebook, gathered activations, signed-activation tables.
+  const u32x4 cw = __builtin_amdgcn_raw_buffer_load_b128(cb_rs, tid * 16, 0, 0);
+  uint32_t src[kColsPerThread];
+#pragma unroll
+  for (int i = 0; i < kColsPerThread; ++i)
+    src[i] = __builtin_amdgcn_raw_buffer_load_b32(pi_rs, (tid + i * kThreads) * 4, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  const uint32_t last = (uint32_t)J.d_in - 1u;  // an out-of-range pi entry is clamped
+  // identity when pi is absent, as a lane mask rather than a branch
+  uint32_t use_pi = R.pi ? ~0u : 0u;
+  asm volatile("" : "+v"(use_pi));
   uint16_t* xp = reinterpret_cast<uint16_t*>(smem + xp_offset<L>(J.gs));
-  {
-    // one load per codeword, then its 16 lane-swizzled replicas
-    const uint4* cbg = reinterpret_cast<const uint4*>(R.codebook);
-    for (int z = tid; z < (int)C::kK; z += kThreads) {
-      const uint4 cw = cbg[z];
+  GroupRegs g[kMaxGroupsPerSplit];
+  if constexpr (kWholeX) {
+    // The whole activation vector is staged in LDS next to pi, so the gather x[pi[p]] is an LDS
+    // read instead of a second dependent trip to memory.
+    constexpr int kChunks = kWholeXMax / 8 / kThreads;  // 16-byte chunks per thread
+    u32x4 xc[kChunks];
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i)
+      xc[i] = __builtin_amdgcn_raw_buffer_load_b128(x_rs, (tid + i * kThreads) * 16, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);  // keep the issue order: the counters wait in order
+#pragma unroll
+    for (int k = 0; k < kMaxGroupsPerSplit; ++k) load_group(g[k], w_rs, k * kBlockBytes, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    uint16_t* xw = xp + kMaxGroupsPerSplit * kGroupCols;  // whole x after the gathered columns
+    const int nchunks = J.d_in / 8;
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i)
+      if (tid + i * kThreads < nchunks)
+        *reinterpret_cast<u32x4*>(xw + (tid + i * kThreads) * 8) = xc[i];
+    if (tid < (int)C::kK) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        *reinterpret_cast<uint4*>(smem + C::kCbOff + z * 256 + r * 16) = cw;
+        *reinterpret_cast<u32x4*>(smem + C::kCbOff + tid * 256 + r * 16) = cw;
     }
-    const uint16_t* x = J.x + (int64_t)inst * J.x_stride;
-    const int c0 = g0 * kGroupCols;
-    const uint32_t last = (uint32_t)J.d_in - 1u;  // an out-of-range pi entry is clamped
-    for (int p = tid; p < ngl * kGroupCols; p += kThreads) {
-      const int col = c0 + p;
-      xp[p] = x[R.pi ? min((uint32_t)R.pi[col], last) : (uint32_t)col];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kColsPerThread; ++i) {
+      const int p = tid + i * kThreads;
+      const uint32_t col = (min(src[i], last) & use_pi) | ((uint32_t)(c0 + p) & ~use_pi);
+      if (p < cols) xp[p] = xw[col];
     }
+  } else {
+    // Wide inputs: pi first, then the gathered activations straight from memory.
+#pragma unroll
+    for (int k = 0; k < kMaxGroupsPerSplit / 2; ++k) load_group(g[k], w_rs, k * kBlockBytes, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    uint16_t xv[kColsPerThread];
+#pragma unroll
+    for (int i = 0; i < kColsPerThread; ++i) {
+      const uint32_t ident = (uint32_t)(c0 + tid + i * kThreads);
+      const uint32_t col = (min(src[i], last) & use_pi) | (ident & ~use_pi);
+      xv[i] = __builtin_amdgcn_raw_buffer_load_b16(x_rs, col * 2u, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = kMaxGroupsPerSplit / 2; k < kMaxGroupsPerSplit; ++k)
+      load_group(g[k], w_rs, k * kBlockBytes, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    if (tid < (int)C::kK) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        *reinterpret_cast<u32x4*>(smem + C::kCbOff + tid * 256 + r * 16) = cw;
+    }
+#pragma unroll
+    for (int i = 0; i < kColsPerThread; ++i)
+      if (tid + i * kThreads < cols) xp[tid + i * kThreads] = xv[i];
   }
   __syncthreads();
+  // 2. Signed-activation tables of the workgroup's columns.
   for (int e = tid; e < ngl * kSubPerGroup * 16; e += kThreads) {
     const int step = e >> 4;
     const uint32_t n = (uint32_t)(e & 15);
@@ -236,16 +289,11 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int i
   float acc = 0.0f;
   const uint32_t laneoff = (uint32_t)(lane & 15) * 16u;
   const uint32_t expo = C::kExpo;
-  if (tile_ok) {
-#define SAGE_GROUP(k)                                                              \
-    if (k < ngl) {                                                                 \
-      if (k + 2 < ngl) load_group(ring[(k + 2) % 3], blk0 + (k + 2) * kBlockBytes, lane); \
-      acc = group_dot<L, k>(ring[k % 3], laneoff, expo, acc);                      \
-    }
-    SAGE_GROUP(0) SAGE_GROUP(1) SAGE_GROUP(2) SAGE_GROUP(3)
-    SAGE_GROUP(4) SAGE_GROUP(5) SAGE_GROUP(6) SAGE_GROUP(7)
+#define SAGE_GROUP(k) \
+  if (k < ngl) acc = group_dot<L, k>(g[k], laneoff, expo, acc);
+  SAGE_GROUP(0) SAGE_GROUP(1) SAGE_GROUP(2) SAGE_GROUP(3)
+  SAGE_GROUP(4) SAGE_GROUP(5) SAGE_GROUP(6) SAGE_GROUP(7)
 #undef SAGE_GROUP
-  }
 
   // 4. Output: direct, or split-K partials reduced by the last workgroup of the row-tile group.
   const int row = rt * kTileRows + lane;
@@ -278,8 +326,8 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int i
   if (tid == 0) counter_reset(counter);
 }
 
-template <int W>
-__global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(3, 8)))
+template <bool kWholeX>
+__global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 8)))
 gemv_kernel(JobTable T) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int wg = blockIdx.x;
@@ -307,11 +355,11 @@ gemv_kernel(JobTable T) {
     R.L = J.log2K;
   }
   switch (R.L) {
-    case 4: gemv_body<4, W>(R, J, inst, wgrow, split, smem); break;
-    case 5: gemv_body<5, W>(R, J, inst, wgrow, split, smem); break;
-    case 6: gemv_body<6, W>(R, J, inst, wgrow, split, smem); break;
-    case 7: gemv_body<7, W>(R, J, inst, wgrow, split, smem); break;
-    default: gemv_body<8, W>(R, J, inst, wgrow, split, smem); break;
+    case 4: gemv_body<4, kWaves, kWholeX>(R, J, inst, wgrow, split, smem); break;
+    case 5: gemv_body<5, kWaves, kWholeX>(R, J, inst, wgrow, split, smem); break;
+    case 6: gemv_body<6, kWaves, kWholeX>(R, J, inst, wgrow, split, smem); break;
+    case 7: gemv_body<7, kWaves, kWholeX>(R, J, inst, wgrow, split, smem); break;
+    default: gemv_body<8, kWaves, kWholeX>(R, J, inst, wgrow, split, smem); break;
   }
 }
 
@@ -320,35 +368,34 @@ gemv_kernel(JobTable T) {
 // ------------------------------------------------------------------------------------------------
 // Host planning
 
-size_t lds_bytes(int maxL, int gs) {
-  // the largest layout among the splits a launch may meet (see SplitC / xp_offset)
+size_t lds_bytes(int maxL, int gs, int whole_d_in) {
+  // the largest layout among the splits a launch may meet (see SplitC / xp_offset): codebook
+  // replicas and tables, the gathered columns (room for the largest split), then whole x if staged
   size_t need = 0;
   for (int L = 4; L <= maxL; ++L) {
-    const size_t b = (L == 8) ? (size_t)32768 + 65536 + (size_t)gs * kGroupCols * 2
-                              : ((size_t)1 << L) * 256 + (size_t)gs * kSubPerGroup * 256 +
-                                    (size_t)gs * kGroupCols * 2;
+    const size_t b = (L == 8) ? (size_t)32768 + 65536
+                              : ((size_t)1 << L) * 256 + (size_t)gs * kSubPerGroup * 256;
     if (b > need) need = b;
   }
+  need += (size_t)kMaxGroupsPerSplit * kGroupCols * 2 + (size_t)whole_d_in * 2;
   return need;
 }
 
-// Launch plan shared by every job of one launch: wavefronts per workgroup and groups per split.
+// Launch plan shared by every job of one launch: column groups per split.
 struct LaunchPlan {
-  int waves;
   int gs;
 };
 
-LaunchPlan plan_launch(int64_t total_blocks, int64_t total_row_tiles) {
-  // Four row tiles per workgroup, so three workgroups fit a compute unit at once and every launch
+LaunchPlan plan_launch(int64_t total_blocks) {
+  // Four row tiles per workgroup, so two workgroups fit a compute unit at once and every launch
   // runs in a single round; groups per split grow until the launch would drop below one
   // workgroup per compute unit (more groups per split = fewer split-K partials to combine).
-  (void)total_row_tiles;
   const int64_t target = (int64_t)device_cu_count();
   for (int gs = kMaxGroupsPerSplit; gs > 1; --gs) {
-    const int64_t wgs = (total_blocks + 4 * gs - 1) / (4 * gs);
-    if (wgs >= target) return LaunchPlan{4, gs};
+    const int64_t wgs = (total_blocks + kWaves * gs - 1) / (kWaves * gs);
+    if (wgs >= target) return LaunchPlan{gs};
   }
-  return LaunchPlan{4, 1};
+  return LaunchPlan{1};
 }
 
 void plan_job(Job& J, int d_out, int d_in, const LaunchPlan& P, int instances) {
@@ -356,7 +403,7 @@ void plan_job(Job& J, int d_out, int d_in, const LaunchPlan& P, int instances) {
   J.d_in = d_in;
   J.rt = ceil_div(d_out, kTileRows);
   J.ng = d_in / kGroupCols;
-  J.wgr = ceil_div(J.rt, P.waves);
+  J.wgr = ceil_div(J.rt, kWaves);
   J.gs = P.gs < J.ng ? P.gs : J.ng;
   J.S = ceil_div(J.ng, J.gs);
   J.gs = ceil_div(J.ng, J.S);
@@ -376,6 +423,9 @@ int finish_and_launch(JobTable& T, void* ws, size_t ws_bytes, hipStream_t stream
   size_t need = 0;
   int wg = 0;
   size_t lds = 0;
+  // whole-x staging when every input of the launch fits
+  bool whole = true;
+  for (int i = 0; i < T.n; ++i) whole = whole && T.jobs[i].d_in <= kWholeXMax;
   for (int i = 0; i < T.n; ++i) {
     Job& J = T.jobs[i];
     const size_t bytes = job_workspace_bytes(J);
@@ -392,7 +442,7 @@ int finish_and_launch(JobTable& T, void* ws, size_t ws_bytes, hipStream_t stream
     J.wg_begin = wg;
     T.wg_begin[i] = wg;
     wg += J.wg_per_inst * J.inst;
-    const size_t l = lds_bytes(maxL, J.gs);
+    const size_t l = lds_bytes(maxL, J.gs, whole ? J.d_in : 0);
     if (l > lds) lds = l;
   }
   for (int i = T.n; i < kMaxJobs; ++i) T.wg_begin[i] = 0x7FFFFFFF;
@@ -402,17 +452,17 @@ int finish_and_launch(JobTable& T, void* ws, size_t ws_bytes, hipStream_t stream
   if (wg == 0) return SAGE_OK;
   static bool attr_done = false;
   if (!attr_done) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_kernel<4>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_kernel<true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess ||
-        hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_kernel<8>),
+        hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_kernel<false>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
       return SAGE_ERR_HIP;
     attr_done = true;
   }
-  if (T.waves == 8)
-    hipLaunchKernelGGL(gemv_kernel<8>, dim3(wg), dim3(8 * 64), lds, stream, T);
+  if (whole)
+    hipLaunchKernelGGL(gemv_kernel<true>, dim3(wg), dim3(kWaves * 64), lds, stream, T);
   else
-    hipLaunchKernelGGL(gemv_kernel<4>, dim3(wg), dim3(4 * 64), lds, stream, T);
+    hipLaunchKernelGGL(gemv_kernel<false>, dim3(wg), dim3(kWaves * 64), lds, stream, T);
   return hip_status();
 }
 
@@ -438,13 +488,10 @@ void direct_job(Job& J, const sage_matrix_t* m, const LaunchPlan& P) {
 }
 
 LaunchPlan plan_for(const sage_matrix_t* mats, int n, int instances = 1) {
-  int64_t blocks = 0, tiles = 0;
-  for (int i = 0; i < n; ++i) {
-    const int64_t rt = ceil_div(mats[i].d_out, kTileRows);
-    blocks += (int64_t)instances * rt * (mats[i].d_in / kGroupCols);
-    tiles += (int64_t)instances * rt;
-  }
-  return plan_launch(blocks, tiles);
+  int64_t blocks = 0;
+  for (int i = 0; i < n; ++i)
+    blocks += (int64_t)instances * ceil_div(mats[i].d_out, kTileRows) * (mats[i].d_in / kGroupCols);
+  return plan_launch(blocks);
 }
 
 }  // namespace
@@ -499,7 +546,6 @@ int sage_gemv_multi(const sage_matrix_t* mats, const uint16_t* const* xs, uint16
   JobTable T{};
   T.n = n;
   const LaunchPlan P = plan_for(mats, n);
-  T.waves = P.waves;
   int maxL = 4;
   for (int i = 0; i < n; ++i) {
     direct_job(T.jobs[i], &mats[i], P);
@@ -550,7 +596,6 @@ int sage_moe_gemv(const sage_matrix_t* experts_dev, int n_experts, const sage_ma
   const LaunchPlan P = plan_for(shapes, n_mats, n_sel);
   JobTable T{};
   T.n = n_mats;
-  T.waves = P.waves;
   for (int j = 0; j < n_mats; ++j) {
     Job& J = T.jobs[j];
     J = Job{};

@@ -5,9 +5,10 @@
 
 namespace sage {
 
-constexpr int kMaxWaves = 8;                  // row tiles per workgroup: 4 or 8 per launch
+constexpr int kWaves = 4;                     // row tiles (wavefronts) per workgroup
 constexpr int kMaxGroupsPerSplit = 8;         // column groups one workgroup handles
 constexpr int kMaxJobs = 16;
+constexpr int kWholeXMax = 16384;           // inputs up to this width are staged whole in LDS
 
 // One product y = W x, possibly repeated over `inst` instances (routed experts). The matrix comes
 // either from the direct fields or, when `table` is set, from table[ids[instance]*tstride + toff]
@@ -28,7 +29,7 @@ struct Job {
   int32_t tstride, toff, n_experts;
   int32_t log2K;
   int32_t d_out, d_in;
-  int32_t rt, ng, wgr;     // row tiles, column groups, workgroup rows (= ceil(rt / waves))
+  int32_t rt, ng, wgr;     // row tiles, column groups, workgroup rows (= ceil(rt / kWaves))
   int32_t S, gs;           // column splits and groups per split
   int32_t wg_begin, wg_per_inst, inst;
   int32_t counters_stride;
@@ -36,7 +37,6 @@ struct Job {
 
 struct JobTable {
   int32_t wg_begin[kMaxJobs];  // first workgroup of each job (unused entries: INT32_MAX)
-  int32_t waves;               // row tiles (wavefronts) per workgroup
   int32_t n;
   int32_t total_wg;
   Job jobs[kMaxJobs];

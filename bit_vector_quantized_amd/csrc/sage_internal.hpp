@@ -91,6 +91,15 @@ int check_matrix(const sage_matrix_t* m);   // shape, split, pointers, alignment
 int hip_status();                            // SAGE_ERR_HIP if the last launch failed
 int device_cu_count();                       // compute units of the current device (cached)
 
+// Global-memory view of a device pointer. Pointers read from memory (descriptor tables) are
+// generic, and loads through them compile to flat instructions, which count against both the
+// vector-memory and the LDS wait counters: every LDS wait would then also wait for the HBM stream.
+// Loads through this view are global loads, counted by vmcnt alone.
+template <typename T>
+__device__ inline const __attribute__((address_space(1))) T* gview(const T* p) {
+  return (const __attribute__((address_space(1))) T*)(p);
+}
+
 // Cross-workgroup hand-off of split-K partials without cache-wide fences. Partials are written with
 // agent-scope relaxed atomic stores (coherent stores, sc1) and read back the same way; each wave
 // waits for its stores to be acknowledged before the workgroup barrier that precedes the counter
