@@ -5,14 +5,20 @@
 
 namespace sage {
 
-constexpr int kWaves = 4;                     // row tiles (wavefronts) per workgroup
-constexpr int kMaxGroupsPerSplit = 8;         // column groups one workgroup handles
+// Workgroup shape: kTiles row tiles x kParts column parts, one wavefront each. The kParts waves of
+// a row tile split the workgroup's columns and add their partial sums in LDS.
+constexpr int kTiles = 4;
+constexpr int kParts = 4;
+constexpr int kWaves = kTiles * kParts;
+constexpr int kThreads = kWaves * 64;
+constexpr int kMaxGroupsPerSplit = 8;                         // column groups per workgroup
+constexpr int kMaxUnits = 2 * kMaxGroupsPerSplit / kParts;    // half-groups per wavefront
 constexpr int kMaxJobs = 16;
-constexpr int kWholeXMax = 16384;           // inputs up to this width are staged whole in LDS
+constexpr int kWholeXMax = 16384;  // inputs up to this width are staged whole in LDS
 
-// One product y = W x, possibly repeated over `inst` instances (routed experts). The matrix comes
-// either from the direct fields or, when `table` is set, from table[ids[instance]*tstride + toff]
-// in device memory.
+// One launch piece: row tiles [tile0, tile0 + rt) of a product y = W x, possibly repeated over
+// `inst` instances (routed experts). The matrix comes either from the direct fields or, when
+// `table` is set, from table[ids[instance] * tstride + toff] in device memory.
 struct Job {
   const uint8_t* packed;
   const uint16_t* codebook;
@@ -21,27 +27,26 @@ struct Job {
   const int32_t* ids;
   const uint16_t* x;
   uint16_t* y;
-  float* partial;
-  uint32_t* counters;
-  int64_t x_stride;        // elements between the inputs of consecutive instances
-  int64_t y_stride;        // elements between the outputs of consecutive instances
-  int64_t partial_stride;  // floats of split-K partials per instance
+  float* partial;           // split-K partials [inst][S][rt * 64]
+  uint32_t* counters;       // arrival counters [inst][rq]
+  int64_t x_stride;         // elements between the inputs of consecutive instances
+  int64_t y_stride;         // elements between the outputs of consecutive instances
+  int64_t partial_stride;   // floats of split-K partials per instance
   int32_t tstride, toff, n_experts;
   int32_t log2K;
-  int32_t d_out, d_in;
-  int32_t rt, ng, wgr;     // row tiles, column groups, workgroup rows (= ceil(rt / kWaves))
-  int32_t S, gs;           // column splits and groups per split
-  int32_t wg_begin, wg_per_inst, inst;
+  int32_t d_out, d_in;      // the whole matrix
+  int32_t tile0, rt, rq;    // first row tile, row tiles, row quads (ceil(rt / kTiles)) of the piece
+  int32_t ng;               // column groups of the matrix
+  int32_t S, gs;            // column splits and groups per split
+  int32_t wg_per_inst, inst;
   int32_t counters_stride;
 };
 
+// Kernel argument: blockIdx.y selects the piece, blockIdx.x the workgroup inside it.
 struct JobTable {
-  int32_t wg_begin[kMaxJobs];  // first workgroup of each job (unused entries: INT32_MAX)
-  int32_t n;
-  int32_t total_wg;
   Job jobs[kMaxJobs];
 };
 
-static_assert(sizeof(JobTable) <= 3072, "kernel argument block too large");
+static_assert(sizeof(JobTable) <= 4096, "kernel argument block too large");
 
 }  // namespace sage

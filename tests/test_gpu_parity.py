@@ -240,6 +240,59 @@ def test_gemv_zero_input_and_zero_grid():
     assert np.all(_np(y) == 0)
 
 
+def test_gemv_wide_input_gathers_from_memory():
+    """d_in above the width staged whole in LDS: the kernel gathers x[pi[p]] from memory."""
+    import torch
+    rng = W.rng_for(134)
+    c = W.draw_codes(rng, 200, 17408, 64, 4)
+    x = W.draw_x(rng, (17408,))
+    p = upload_pack(c)
+    y = sage.gemv(p, torch.from_numpy(x).cuda())
+    check_gemv("wide 200x17408", c, x, y)
+
+
+def test_gemv_input_not_16_byte_aligned():
+    """x only 4-byte aligned (an offset view): the kernel must not stage it with 16-byte loads."""
+    import torch
+    rng = W.rng_for(135)
+    c = W.draw_codes(rng, 300, 1024, 32, 5)
+    x = W.draw_x(rng, (1024,))
+    buf = torch.zeros(1024 + 2, dtype=torch.float16, device="cuda")
+    buf[2:] = torch.from_numpy(x).cuda()
+    xd = buf[2:]
+    assert xd.data_ptr() % 16 != 0 and xd.data_ptr() % 4 == 0
+    p = upload_pack(c)
+    y = sage.gemv(p, xd)
+    check_gemv("x at a 4-byte offset", c, x, y)
+
+
+def test_gemv_identity_permutation():
+    """pi absent (NULL): columns are taken in stored order."""
+    import dataclasses
+    import torch
+    rng = W.rng_for(136)
+    c = W.draw_codes(rng, 130, 768, 64, 4)
+    c.pi = np.arange(768, dtype=np.int32)
+    x = W.draw_x(rng, (768,))
+    p = dataclasses.replace(upload_pack(c), pi=None)
+    y = sage.gemv(p, torch.from_numpy(x).cuda())
+    check_gemv("pi = NULL", c, x, y)
+
+
+def test_gemv_multi_sixteen_mixed_products():
+    """The most products one launch takes, of very different sizes (cut into launch pieces)."""
+    import torch
+    rng = W.rng_for(137)
+    shapes = [(64 * (1 + (i * 7) % 23), 128 * (1 + i % 5)) for i in range(16)]
+    splits = [(16, 6), (32, 5), (64, 4), (128, 3), (256, 2)]
+    cs = [W.draw_codes(rng, d_out, d_in, *splits[i % 5]) for i, (d_out, d_in) in enumerate(shapes)]
+    xs = [W.draw_x(rng, (d_in,)) for _, d_in in shapes]
+    ps = [upload_pack(c) for c in cs]
+    ys = sage.gemv_multi(ps, [torch.from_numpy(x).cuda() for x in xs])
+    for i, (c, x, y) in enumerate(zip(cs, xs, ys)):
+        check_gemv(f"mixed[{i}] {c.d_out}x{c.d_in} K={c.K}", c, x, y)
+
+
 # ------------------------------------------------------------------------------ small-batch gemm
 
 def check_gemm(name, c, X, Y_dev, W_hat=None):
