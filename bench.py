@@ -21,7 +21,6 @@ from __future__ import annotations
 
 import argparse
 import hashlib
-import glob
 import json
 import math
 import os
@@ -92,10 +91,14 @@ def packed_weight_bytes(p):
     return p.d_out * p.d_in * 18 // 64 + p.d_out * (p.d_in // 128) * 4
 
 
+GEMV_SOURCES = ("sage_gemv.hip", "sage_gemv.hpp", "sage_internal.hpp")
+
+
 def kernel_sources_digest():
+    """sha256 (16 hex digits) over the sources the batch-one kernel is built from."""
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "bit_vector_quantized_amd", "csrc", "*"))):
-        with open(f, "rb") as fh:
+    for name in GEMV_SOURCES:
+        with open(os.path.join(ROOT, "bit_vector_quantized_amd", "csrc", name), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -237,6 +240,50 @@ def dominant_graph(bench, count, evs):
     torch.cuda.synchronize()
     per = a.elapsed_time(b) / (reps * count)
     return [per] * count
+
+
+def stream_reference(nbytes):
+    """The floor for one streaming launch of `nbytes`: sage_stream_read (plain 16-byte loads, no
+    decode) over consecutive windows of a 1 GiB buffer, one launch per window, in a graph timed
+    like the dominant launch; plus one launch reading the whole GiB."""
+    import torch
+    import bit_vector_quantized_amd as sage
+    pool = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    n = (nbytes + 15) // 16 * 16
+    windows = (1 << 30) // n
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for w in range(windows):
+                sage.stream_read(pool[w * n:(w + 1) * n], sink=sink)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    reps = 5
+    with torch.cuda.stream(s):
+        g.replay()
+        a.record(s)
+        for _ in range(reps):
+            g.replay()
+        b.record(s)
+        torch.cuda.synchronize()
+        c = torch.cuda.Event(enable_timing=True)
+        d = torch.cuda.Event(enable_timing=True)
+        sage.stream_read(pool, sink=sink)
+        c.record(s)
+        for _ in range(reps):
+            sage.stream_read(pool, sink=sink)
+        d.record(s)
+    torch.cuda.synchronize()
+    per_us = a.elapsed_time(b) * 1e3 / (reps * windows)
+    gib_us = c.elapsed_time(d) * 1e3 / reps
+    del pool
+    return {"bytes_per_launch": n, "us_per_launch": round(per_us, 3),
+            "gbs": round(n / (per_us * 1e-6) / 1e9, 1),
+            "one_gib_launch_gbs": round((1 << 30) / (gib_us * 1e-6) / 1e9, 1)}
 
 
 # ------------------------------------------------------------------------------------------------
@@ -457,6 +504,11 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    log("[bench] timing the streaming-read reference")
+    ref = stream_reference(bench.dom_bytes)
+    if roofline is not None:
+        roofline["stream_read_reference"] = ref
+        roofline["frac_of_stream_read"] = round(roofline["achieved"] / ref["gbs"], 4)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         line["cpu_baseline"] = cpu_baseline(bench.layer, args.cpu_seconds)

@@ -65,6 +65,7 @@ _SIGNATURES = {
     "sage_gemm_small": (_I, [_PM, _P, _I, _I, _P, _I, _P, _SZ, _P]),
     "sage_moe_gemv_workspace_bytes": (_I, [_PM, _I, _I, _PSZ]),
     "sage_moe_gemv": (_I, [_PM, _I, _PM, _I, _P, _I, _PP, _PI64, _PP, _PI64, _P, _SZ, _P]),
+    "sage_stream_read": (_I, [_P, _SZ, _P, _P]),
 }
 
 
@@ -311,3 +312,18 @@ def moe_gemv(table, n_experts: int, shapes: Sequence[tuple], ids, xs, x_strides,
         ctypes.cast(_ptr(table), _PM), n_experts, sh, n_mats, _ptr(ids), ids.numel(), xa, xsa,
         ya, ysa, _ptr(ws), ws.numel(), _stream(stream)))
     return ys
+
+
+def stream_read(buf, nbytes: Optional[int] = None, sink=None, stream=None):
+    """Measurement helper: one launch that reads `nbytes` (default: all) bytes of a device tensor
+    once (see sage_stream_read in include/sage.h)."""
+    torch = _torch()
+    _require_cuda(buf)
+    total = buf.numel() * buf.element_size()
+    n = total if nbytes is None else nbytes
+    if n > total:
+        raise ValueError("nbytes exceeds the buffer")
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    _check("sage_stream_read", lib().sage_stream_read(_ptr(buf), n, _ptr(sink), _stream(stream)))
+    return sink

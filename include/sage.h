@@ -173,6 +173,19 @@ int sage_moe_gemv(const sage_matrix_t* experts_dev, int n_experts, const sage_ma
                   const int64_t* x_strides, uint16_t* const* ys, const int64_t* y_strides,
                   void* ws, size_t ws_bytes, sage_stream_t stream);
 
+/* ------------------------------------------------------------------------------------------
+ * sage_stream_read: measurement helper, not part of the decode path. Reads `bytes` bytes at `p`
+ * once, in one launch, with the same 16-byte non-temporal buffer loads the decode kernels use for
+ * packed weights, and writes nothing unless the data XOR-reduces to a fixed improbable value (then
+ * one uint32 goes to *sink). Its time is the floor a single streaming launch of that size can
+ * reach on this device (launch, wave dispatch and first-data latency included), the reference
+ * against which the decode kernels' launch times are read.
+ *   p      device buffer, 16-byte aligned; bytes a multiple of 16 (0 launches nothing).
+ *   sink   device uint32 [1].
+ * Errors: SAGE_ERR_NULL, SAGE_ERR_ALIGN (p not 16-byte aligned or bytes % 16 != 0), SAGE_ERR_HIP.
+ */
+int sage_stream_read(const void* p, size_t bytes, uint32_t* sink, sage_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -115,3 +115,12 @@ def test_moe_validation(L):
     assert L.sage_moe_gemv(tab, 128, shapes, 3, ids, 8, xs, xst, ys, small_y, None, 0, None) == ARG
     n = ctypes.c_size_t(0)
     assert L.sage_moe_gemv_workspace_bytes(shapes, 3, 8, ctypes.byref(n)) == OK
+
+
+def test_stream_read_validation(L):
+    sink = ctypes.c_void_p(1 << 20)
+    assert L.sage_stream_read(None, 16, sink, None) == NULL
+    assert L.sage_stream_read(ctypes.c_void_p(1 << 21), 16, None, None) == NULL
+    assert L.sage_stream_read(ctypes.c_void_p((1 << 21) + 8), 16, sink, None) == ALIGN
+    assert L.sage_stream_read(ctypes.c_void_p(1 << 21), 24, sink, None) == ALIGN
+    assert L.sage_stream_read(ctypes.c_void_p(1 << 21), 0, sink, None) == OK

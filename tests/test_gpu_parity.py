@@ -374,3 +374,12 @@ def test_moe_gemv(splits):
         check_gemv(f"moe e{int(e)}.gate", ex["gate"], moe.x, yg[s])
         check_gemv(f"moe e{int(e)}.up", ex["up"], moe.x, yu[s])
         check_gemv(f"moe e{int(e)}.down", ex["down"], moe.h[s], yd[s])
+
+
+def test_stream_read_reference_runs():
+    """The measurement helper reads a buffer (including a ragged last workgroup) and writes nothing."""
+    import torch
+    buf = torch.ones(3 * 65536 + 160, dtype=torch.uint8, device="cuda")
+    sink = sage.stream_read(buf)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0
