@@ -1,27 +1,40 @@
 // Small-batch product Y = X W_hat^T for SAGE-packed weights on gfx950 matrix cores (SAGE paper §3.5
 // and App. A.1: each weight is decoded once per output tile and reused across the activation rows).
 //
-// A workgroup owns one 64-row tile of W (16 rows per wavefront), one range of column groups and one
-// chunk of up to 64 activation rows. The wavefront computes D = A * B with
+// MFMA mapping. A wavefront owns 16 weight rows and computes D = A * B with
 // v_mfma_f32_16x16x32_f16: B is 32 input channels x 16 weight rows, A is 16 activation rows x the
 // same 32 channels. In the B operand a lane supplies 8 consecutive input channels of one weight row,
 // which is exactly one subvector, so the lane decodes its subvector straight into the operand:
-// w_i = r_hat * (+-c_z,i), r_hat = mu + q*delta computed in fp32, the product formed in fp16. The
-// activations are gathered through pi into LDS once per workgroup (§3.2) and read as the A operand.
-// Lanes 16u..16u+15 of MFMA step kk supply subvector 4u + kk of their row, so A reads the same
-// channels; the channel order inside the 32-wide contraction is the same for A and B.
+// w_i = r_hat * (+-c_z,i), r_hat = mu + q*delta computed in fp32, the product formed in fp16. Lanes
+// 16u..16u+15 of MFMA step kk supply subvector 4u + kk of their row, so A reads the same channels;
+// the channel order inside the 32-wide contraction is the same for A and B. One decoded subvector
+// feeds NT = 1, 2 or 4 MFMAs (16, 32 or 64 activation rows).
+//
+// Workgroup: 16 wavefronts = 2 weight tiles of 64 rows (4 waves of 16 rows each) x 2 column parts.
+// It owns a range of column groups (split-K over workgroups) and one chunk of activation rows; the
+// activations of its columns are staged once in LDS (gathered through pi, §3.2) and shared by both
+// tiles, the two column parts add their accumulators in LDS. All packed-weight loads of a wave are
+// issued up front through range-checked buffer loads, as in the batch-one kernel.
 #include "sage_internal.hpp"
 
 namespace sage {
 namespace {
 
-constexpr int kGemmWaves = 4;
-constexpr int kGemmThreads = kGemmWaves * 64;
-constexpr int kMaxGS = 8;        // column groups per split
+constexpr int kGTiles = 2;                           // 64-row weight tiles per workgroup
+constexpr int kGParts = 2;                           // column parts
+constexpr int kGWaves = kGTiles * 4 * kGParts;       // 16
+constexpr int kGThreads = kGWaves * 64;              // 1024
+constexpr int kGMaxGS = 8;                           // column groups per split
+constexpr int kGMaxUnits = kGMaxGS / kGParts;        // groups per wavefront
+constexpr int kPermuteMinRows = 8;                   // from this many rows on, X is permuted once
+constexpr int kDirectRows = kPermuteMinRows;         // rows gathered straight from X below that
+constexpr uint32_t kNowhere = 1u << 30;              // an offset past every range
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct GemmArgs {
   const uint8_t* packed;
@@ -29,16 +42,18 @@ struct GemmArgs {
   const int32_t* pi;
   const uint16_t* X;
   uint16_t* Y;
-  float* partial;
-  uint32_t* counters;
+  float* partial;       // [mchunk][split][mrows_chunk][rt * 64]
+  uint32_t* counters;   // [mchunk][rpairs]
   int64_t ldx, ldy;
   int32_t d_out, d_in, M, L;
-  int32_t rt, ng, S, gs, mchunks;
-  int32_t mrows_chunk;  // activation rows per workgroup = 16 * tiles
-  int32_t vec_x;        // X rows are 16-byte aligned and already in permuted order
+  int32_t rt, rpairs, ng, S, gs, mchunks;
+  int32_t mrows_chunk;  // activation rows per workgroup = 16 * NT
+  int32_t vec_x;        // X rows are 16-byte aligned and already in permuted order (kVec)
 };
 
-constexpr int kPermuteMinRows = 8;  // from this many rows on, X is permuted once per call
+__device__ inline __amdgpu_buffer_rsrc_t view(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
 
 // Sign masks of one nibble: bits 0/1 -> signs of the first fp16 pair, bits 2/3 -> second pair.
 __device__ inline uint2 nibble_masks(uint32_t n) {
@@ -65,128 +80,172 @@ __device__ inline uint32_t mul_pair(uint32_t c, half2_t r) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-template <int L, int NT>
-__device__ void gemm_body(const GemmArgs& A, int rt, int split, int mchunk, uint8_t* smem) {
+// LDS layout: codebook replicas [K][16][16 B], sign-mask table [16][8 B], flag, then the X tile
+// [NT*16][gs*128 + 8] fp16 (also the part-sum exchange once the products are done).
+__host__ __device__ inline uint32_t gemm_xs_offset(int L) { return (1u << L) * 256u + 144u; }
+
+template <int L, int NT, bool kVec>
+__device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint8_t* smem) {
   constexpr uint32_t kK = 1u << L;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int j = lane & 15;      // weight row inside the wave's 16
-  const int u = lane >> 4;      // channel quadrant
+  const int j = lane & 15;                 // weight row inside the wave's 16 (B), X row (A)
+  const int u = lane >> 4;                 // channel quadrant
+  const int quarter = wave % (kGTiles * 4);
+  const int part = wave / (kGTiles * 4);
+  const int rt = rp * kGTiles + quarter / 4;
+  const bool tile_ok = rt < A.rt;
+  const int wrow_in_tile = (quarter % 4) * 16 + j;
+  const int wrow = rt * kTileRows + wrow_in_tile;
   const int g0 = split * A.gs;
   const int ngl = min(A.ng - g0, A.gs);
+  const int gpp = (ngl + kGParts - 1) / kGParts;
+  const int k0 = part * gpp;
+  const int ngp = max(0, min(ngl - k0, gpp));   // groups of this wave
   const int m0 = mchunk * A.mrows_chunk;
   const int mrows = min(A.M - m0, NT * 16);
-  const int wrow_in_tile = wave * 16 + j;
-  const int wrow = rt * kTileRows + wrow_in_tile;
+  const int c0 = g0 * kGroupCols;
+  const int cols = ngl * kGroupCols;
+  const int xstride = A.gs * kGroupCols + 8;     // fp16 elements per staged activation row
 
-  // LDS: codebook replicas [K][16][16 B], sign-mask table [16][8 B], then the X tile
-  // [NT*16][gs*128 (+8 pad)] fp16.
   uint8_t* cb = smem;
   uint2* smask = reinterpret_cast<uint2*>(smem + kK * 256);
-  const int xstride = A.gs * kGroupCols + 8;  // fp16 elements per activation row (padded)
-  _Float16* xs = reinterpret_cast<_Float16*>(smem + kK * 256 + 128);
-  {
-    const uint4* cbg = reinterpret_cast<const uint4*>(A.codebook);
-    for (int z = tid; z < (int)kK; z += kGemmThreads) {
-      const uint4 cw = cbg[z];
+  uint32_t* flag = reinterpret_cast<uint32_t*>(smem + kK * 256 + 128);
+  _Float16* xs = reinterpret_cast<_Float16*>(smem + gemm_xs_offset(L));
+
+  // 1. Loads: codebook, pi, activations, then every packed group of the wave.
+  const __amdgpu_buffer_rsrc_t cb_rs = view(A.codebook, kK * 16u);
+  const u32x4 cw = __builtin_amdgcn_raw_buffer_load_b128(cb_rs, tid * 16, 0, 0);
+  const __amdgpu_buffer_rsrc_t x_rs =
+      view(A.X + (int64_t)m0 * A.ldx, (uint32_t)((int64_t)mrows * A.ldx * 2));
+  constexpr int kVecLoads = 2 * NT;  // 16-byte chunks per thread: NT*16 rows x 128 chunks
+  u32x4 xc[kVecLoads];
+  uint16_t xv[kDirectRows];
+  const int nck = ngl * (kGroupCols / 8);
+  if constexpr (kVec) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) *reinterpret_cast<uint4*>(cb + z * 256 + r * 16) = cw;
+    for (int i = 0; i < kVecLoads; ++i) {
+      const int e = tid + i * kGThreads;
+      const int m = e >> 7, ch = e & 127;
+      const uint32_t off =
+          ch < nck ? (uint32_t)(((int64_t)m * A.ldx + c0 + ch * 8) * 2) : kNowhere;
+      xc[i] = __builtin_amdgcn_raw_buffer_load_b128(x_rs, off, 0, 0);
     }
-    if (tid < 16) smask[tid] = nibble_masks((uint32_t)tid);
-    const int cols = ngl * kGroupCols;
-    const int c0 = g0 * kGroupCols;
-    if (A.vec_x) {
-      // 16-byte chunks of already-permuted rows, eight loads in flight per thread
-      const int chunks = cols / 8;
-      const int total = NT * 16 * chunks;
-      for (int base = 0; base < total; base += 8 * kGemmThreads) {
-        uint4 v[8];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const uint8_t* blk0 = A.packed + ((int64_t)rt * A.ng + g0) * kBlockBytes;
+  const __amdgpu_buffer_rsrc_t w_rs = view(blk0, tile_ok ? (uint32_t)(ngl * kBlockBytes) : 0u);
+  u32x2 pp[kGMaxUnits], sd[kGMaxUnits];
+  const uint32_t plane = (u < 2 ? kPlaneA : kPlaneB) + wrow_in_tile * 16 + (u & 1) * 8;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int e = base + u * kGemmThreads + tid;
-          const int m = e / chunks;
-          v[u] = make_uint4(0, 0, 0, 0);
-          if (e < total && m < mrows)
-            v[u] = *reinterpret_cast<const uint4*>(A.X + (int64_t)(m0 + m) * A.ldx + c0 +
-                                                   (e - m * chunks) * 8);
-        }
+  for (int k = 0; k < kGMaxUnits; ++k) {
+    const bool ok = k < ngp;
+    const uint32_t blk = (uint32_t)(k0 + k) * kBlockBytes;
+    pp[k] = __builtin_amdgcn_raw_buffer_load_b64(w_rs, ok ? blk + plane : kNowhere, 0, 2);
+    sd[k] = __builtin_amdgcn_raw_buffer_load_b64(
+        w_rs, ok ? blk + kSidePlane + wrow_in_tile * 8 : kNowhere, 0, 2);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (!kVec) {
+    // few rows in original order: gather through pi straight from X (rows >= mrows read zeros)
+    const __amdgpu_buffer_rsrc_t pi_rs =
+        view(A.pi ? A.pi + c0 : nullptr, A.pi ? (uint32_t)cols * 4u : 0u);
+    const uint32_t pv = __builtin_amdgcn_raw_buffer_load_b32(pi_rs, tid * 4, 0, 0);
+    const uint32_t src = A.pi ? min(pv, (uint32_t)A.d_in - 1u) : (uint32_t)(c0 + tid);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int e = base + u * kGemmThreads + tid;
-          const int m = e / chunks;
-          if (e < total) *reinterpret_cast<uint4*>(xs + m * xstride + (e - m * chunks) * 8) = v[u];
-        }
-      }
-    } else {
-      for (int e = tid; e < NT * 16 * cols; e += kGemmThreads) {
-        const int m = e / cols;
-        const int p = e - m * cols;
-        _Float16 v = (_Float16)0.0f;
-        if (m < mrows) {
-          const int col = c0 + p;
-          const int src = A.pi ? (int)min((uint32_t)A.pi[col], (uint32_t)A.d_in - 1u) : col;
-          v = __builtin_bit_cast(_Float16, A.X[(int64_t)(m0 + m) * A.ldx + src]);
-        }
-        xs[m * xstride + p] = v;
-      }
+    for (int m = 0; m < kDirectRows; ++m)
+      xv[m] = __builtin_amdgcn_raw_buffer_load_b16(
+          x_rs, tid < cols ? (uint32_t)(((int64_t)m * A.ldx + src) * 2) : kNowhere, 0, 0);
+  }
+
+  // 2. LDS set-up.
+  if (tid < (int)kK) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) *reinterpret_cast<u32x4*>(cb + tid * 256 + r * 16) = cw;
+  }
+  if (tid < 16) smask[tid] = nibble_masks((uint32_t)tid);
+  if constexpr (kVec) {
+#pragma unroll
+    for (int i = 0; i < kVecLoads; ++i) {
+      const int e = tid + i * kGThreads;
+      const int m = e >> 7, ch = e & 127;
+      if (ch < nck) *reinterpret_cast<u32x4*>(xs + m * xstride + ch * 8) = xc[i];
     }
+  } else if (tid < cols) {
+#pragma unroll
+    for (int m = 0; m < 16; ++m)
+      xs[m * xstride + tid] = m < kDirectRows ? __builtin_bit_cast(_Float16, xv[m]) : (_Float16)0.0f;
   }
   __syncthreads();
 
+  // 3. Decode once, multiply NT times.
   float4_t acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-  const bool row_ok = wrow < A.d_out;  // padded rows decode to zero weights anyway
+  const bool row_ok = tile_ok && wrow < A.d_out;  // padded rows decode to zero weights anyway
   const uint32_t laneoff = (uint32_t)(lane & 15) * 16u;
-  for (int k = 0; k < ngl; ++k) {
-    const uint8_t* blk = A.packed + ((int64_t)rt * A.ng + g0 + k) * kBlockBytes;
-    const uint8_t* plane = blk + (u < 2 ? kPlaneA : kPlaneB);
-    const uint2 pp = *reinterpret_cast<const uint2*>(plane + wrow_in_tile * 16 + (u & 1) * 8);
-    const uint2 side = *reinterpret_cast<const uint2*>(blk + kSidePlane + wrow_in_tile * 8);
-    const float mu = h2f(side.y);
-    const float dl = h2f(side.y >> 16);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      // subvector 4u + kk of the group: payload dword 2u + kk/2, half a (kk even) or b (kk odd)
-      const uint32_t P = (kk < 2) ? pp.x : pp.y;
-      const int pair = 2 * u + (kk >> 1);
-      uint32_t s, f;
-      if ((kk & 1) == 0) {
-        s = ((P >> 4) & 15u) | ((P >> 28) << 4);
-        f = (P >> 8) & 1023u;
-      } else {
-        s = (P & 15u) | (((side.x >> (4 * pair)) & 15u) << 4);
-        f = (P >> 18) & 1023u;
-      }
-      const uint32_t z = f & (kK - 1u);
-      const float r = fmaf((float)(f >> L), dl, mu);
-      const _Float16 rh = (_Float16)r;
-      const half2_t r2 = half2_t{rh, rh};
-      const uint4 c = *reinterpret_cast<const uint4*>(cb + z * 256 + laneoff);
-      const uint2 mlo = smask[s & 15u];
-      const uint2 mhi = smask[s >> 4];
-      uint32_t w[4];
-      w[0] = mul_pair(c.x ^ mlo.x, r2);
-      w[1] = mul_pair(c.y ^ mlo.y, r2);
-      w[2] = mul_pair(c.z ^ mhi.x, r2);
-      w[3] = mul_pair(c.w ^ mhi.y, r2);
-      if (!row_ok) w[0] = w[1] = w[2] = w[3] = 0u;
-      const half8_t b = __builtin_bit_cast(half8_t, make_uint4(w[0], w[1], w[2], w[3]));
-      const int xcol = k * kGroupCols + (4 * u + kk) * 8;
+  for (int k = 0; k < kGMaxUnits; ++k) {
+    if (k < ngp) {
+      const int slot = k0 + k;
+      const float mu = h2f(sd[k][1]);
+      const float dl = h2f(sd[k][1] >> 16);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const half8_t a = *reinterpret_cast<const half8_t*>(xs + (t * 16 + j) * xstride + xcol);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[t], 0, 0, 0);
+      for (int kk = 0; kk < 4; ++kk) {
+        // subvector 4u + kk of the group: payload dword 2u + kk/2, half a (kk even) or b (kk odd)
+        const uint32_t P = (kk < 2) ? pp[k][0] : pp[k][1];
+        const int pair = 2 * u + (kk >> 1);
+        uint32_t s, f;
+        if ((kk & 1) == 0) {
+          s = ((P >> 4) & 15u) | ((P >> 28) << 4);
+          f = (P >> 8) & 1023u;
+        } else {
+          s = (P & 15u) | (((sd[k][0] >> (4 * pair)) & 15u) << 4);
+          f = (P >> 18) & 1023u;
+        }
+        const uint32_t z = f & (kK - 1u);
+        const float r = fmaf((float)(f >> L), dl, mu);
+        const _Float16 rh = (_Float16)r;
+        const half2_t r2 = half2_t{rh, rh};
+        const uint4 c = *reinterpret_cast<const uint4*>(cb + z * 256 + laneoff);
+        const uint2 mlo = smask[s & 15u];
+        const uint2 mhi = smask[s >> 4];
+        uint32_t w[4];
+        w[0] = mul_pair(c.x ^ mlo.x, r2);
+        w[1] = mul_pair(c.y ^ mlo.y, r2);
+        w[2] = mul_pair(c.z ^ mhi.x, r2);
+        w[3] = mul_pair(c.w ^ mhi.y, r2);
+        if (!row_ok) w[0] = w[1] = w[2] = w[3] = 0u;
+        const half8_t b = __builtin_bit_cast(half8_t, make_uint4(w[0], w[1], w[2], w[3]));
+        const int xcol = slot * kGroupCols + (4 * u + kk) * 8;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const half8_t a = *reinterpret_cast<const half8_t*>(xs + (t * 16 + j) * xstride + xcol);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[t], 0, 0, 0);
+        }
       }
     }
   }
 
-  // D layout: lane holds column j (weight row) and activation rows 4u .. 4u+3 of each 16-row tile.
+  // 4. The second column part hands its sums to the first through LDS (the X tile is done).
+  __syncthreads();
+  float4_t* red = reinterpret_cast<float4_t*>(xs);
+  if (part == 1) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) red[(quarter * NT + t) * 64 + lane] = acc[t];
+  }
+  __syncthreads();
+  if (part == 0) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] += red[(quarter * NT + t) * 64 + lane];
+  }
+
+  // 5. Output. D layout: lane holds weight row j and activation rows 4u .. 4u+3 of each tile.
   const int64_t rows_pad = (int64_t)A.rt * kTileRows;
+  const bool out_ok = part == 0 && row_ok;
   if (A.S == 1) {
-    if (row_ok) {
+    if (out_ok) {
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -197,32 +256,29 @@ __device__ void gemm_body(const GemmArgs& A, int rt, int split, int mchunk, uint
     }
     return;
   }
-  // split-K: partial[mchunk][split][m][rows_pad]
-  float* part = A.partial + (int64_t)mchunk * A.S * A.mrows_chunk * rows_pad;
-  if (row_ok) {
+  float* pbuf = A.partial + (int64_t)mchunk * A.S * A.mrows_chunk * rows_pad;
+  if (out_ok) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = t * 16 + 4 * u + r;
         if (m < mrows)
-          store_coherent(part + ((int64_t)split * A.mrows_chunk + m) * rows_pad + wrow, acc[t][r]);
+          store_coherent(pbuf + ((int64_t)split * A.mrows_chunk + m) * rows_pad + wrow, acc[t][r]);
       }
   }
   wait_stores();
   __syncthreads();
-  uint32_t* flag = reinterpret_cast<uint32_t*>(smem);
-  uint32_t* counter = A.counters + (int64_t)mchunk * A.rt + rt;
+  uint32_t* counter = A.counters + (int64_t)mchunk * A.rpairs + rp;
   if (tid == 0) *flag = (counter_add(counter) == (uint32_t)(A.S - 1)) ? 1u : 0u;
   __syncthreads();
   if (*flag == 0u) return;
-  // last workgroup: reduce this row tile for all rows of the chunk. Thread t owns elements
-  // t + 256 i (activation row 4 i + t / 64, tile row t % 64); the partials of four splits are in
-  // flight at a time and summed in split order.
-  constexpr int kPer = NT * 16 * kTileRows / kGemmThreads;
-  const int trow = rt * kTileRows + (tid & 63);
+  // last workgroup: reduce both tiles for all rows of the chunk. Thread t owns elements
+  // t + 1024 i (activation row e / 128, row e % 128 of the tile pair); four splits in flight.
+  constexpr int kPer = NT * 16 * kGTiles * kTileRows / kGThreads;
   const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(
-      part, (uint32_t)((int64_t)A.S * A.mrows_chunk * rows_pad * (int64_t)sizeof(float)));
+      pbuf, (uint32_t)((int64_t)A.S * A.mrows_chunk * rows_pad * (int64_t)sizeof(float)));
+  const int prow = rp * kGTiles * kTileRows + (tid & 127);
   float sum[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) sum[i] = 0.0f;
@@ -232,10 +288,10 @@ __device__ void gemm_body(const GemmArgs& A, int rt, int split, int mchunk, uint
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
-        const int m = 4 * i + (tid >> 6);
+        const int m = (tid >> 7) + 8 * i;
         const int sp = min(sp0 + q, A.S - 1);
         v[q][i] = load_coherent_at(
-            rs, (uint32_t)((((int64_t)sp * A.mrows_chunk + m) * rows_pad + trow) * sizeof(float)));
+            rs, (uint32_t)((((int64_t)sp * A.mrows_chunk + m) * rows_pad + prow) * sizeof(float)));
       }
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -243,30 +299,30 @@ __device__ void gemm_body(const GemmArgs& A, int rt, int split, int mchunk, uint
       for (int i = 0; i < kPer; ++i)
         if (sp0 + q < A.S) sum[i] += v[q][i];
   }
-  if (trow < A.d_out) {
+  if (prow < A.d_out) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int m = 4 * i + (tid >> 6);
-      if (m < mrows) A.Y[(int64_t)(m0 + m) * A.ldy + trow] = f2h(sum[i]);
+      const int m = (tid >> 7) + 8 * i;
+      if (m < mrows) A.Y[(int64_t)(m0 + m) * A.ldy + prow] = f2h(sum[i]);
     }
   }
   if (tid == 0) counter_reset(counter);
 }
 
-template <int NT>
-__global__ void __launch_bounds__(kGemmThreads) gemm_kernel(GemmArgs A) {
+template <int NT, bool kVec>
+__global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs A) {
   extern __shared__ __align__(16) uint8_t smem[];
-  const int per_chunk = A.rt * A.S;
+  const int per_chunk = A.rpairs * A.S;
   const int mchunk = blockIdx.x / per_chunk;
   const int local = blockIdx.x - mchunk * per_chunk;
-  const int rt = local / A.S;
-  const int split = local - rt * A.S;
+  const int rp = local / A.S;
+  const int split = local - rp * A.S;
   switch (A.L) {
-    case 4: gemm_body<4, NT>(A, rt, split, mchunk, smem); break;
-    case 5: gemm_body<5, NT>(A, rt, split, mchunk, smem); break;
-    case 6: gemm_body<6, NT>(A, rt, split, mchunk, smem); break;
-    case 7: gemm_body<7, NT>(A, rt, split, mchunk, smem); break;
-    default: gemm_body<8, NT>(A, rt, split, mchunk, smem); break;
+    case 4: gemm_body<4, NT, kVec>(A, rp, split, mchunk, smem); break;
+    case 5: gemm_body<5, NT, kVec>(A, rp, split, mchunk, smem); break;
+    case 6: gemm_body<6, NT, kVec>(A, rp, split, mchunk, smem); break;
+    case 7: gemm_body<7, NT, kVec>(A, rp, split, mchunk, smem); break;
+    default: gemm_body<8, NT, kVec>(A, rp, split, mchunk, smem); break;
   }
 }
 
@@ -275,24 +331,29 @@ int tiles_for(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
 constexpr size_t kLdsLimit = 160 * 1024;
 
 size_t lds_for(int L, int nt, int gs) {
-  return ((size_t)1 << L) * 256 + 128 + (size_t)nt * 16 * ((size_t)gs * kGroupCols + 8) * 2;
+  const size_t xtile = (size_t)nt * 16 * ((size_t)gs * kGroupCols + 8) * 2;
+  const size_t red = (size_t)kGTiles * 4 * nt * 64 * 16;
+  return gemm_xs_offset(L) + (xtile > red ? xtile : red);
 }
 
+// Groups per split: the fewest that keep the launch within one workgroup per compute unit (a
+// workgroup fills a compute unit) and the LDS budget.
 void plan(GemmArgs& A, int M) {
   A.rt = ceil_div(A.d_out, kTileRows);
+  A.rpairs = ceil_div(A.rt, kGTiles);
   A.ng = A.d_in / kGroupCols;
   A.mrows_chunk = 16 * tiles_for(M);
   A.mchunks = ceil_div(M, A.mrows_chunk);
-  // about 2 workgroups per compute unit in total
-  const int64_t target = (int64_t)device_cu_count() * 2;
-  int64_t s = target / ((int64_t)A.rt * A.mchunks);
-  if (s < 1) s = 1;
-  if (s > A.ng) s = A.ng;
-  A.gs = ceil_div(A.ng, (int)s);
-  if (A.gs > kMaxGS) A.gs = kMaxGS;
-  // keep the codebook replicas plus the activation tile small enough for two workgroups per CU
-  while (A.gs > 1 && lds_for(A.L, tiles_for(M), A.gs) > kLdsLimit / 2) --A.gs;
-  A.S = ceil_div(A.ng, A.gs);
+  const int nt = tiles_for(M);
+  const int64_t cus = device_cu_count();
+  int best = 1;
+  for (int gs = 1; gs <= kGMaxGS && gs <= A.ng; ++gs) {
+    if (lds_for(A.L, nt, gs) > kLdsLimit) break;
+    best = gs;
+    if ((int64_t)A.mchunks * A.rpairs * ceil_div(A.ng, gs) <= cus) break;
+  }
+  A.S = ceil_div(A.ng, best);
+  A.gs = ceil_div(A.ng, A.S);
 }
 
 size_t permuted_bytes(int M, int d_in) {
@@ -303,7 +364,7 @@ size_t workspace_for(const GemmArgs& A) {
   const size_t xp = permuted_bytes(A.M, A.d_in);
   if (A.S == 1) return xp;
   const size_t part = (size_t)A.mchunks * A.S * A.mrows_chunk * A.rt * kTileRows * 4;
-  const size_t cnt = (size_t)A.mchunks * A.rt * 4;
+  const size_t cnt = (size_t)A.mchunks * A.rpairs * 4;
   return xp + (part + cnt + 255) / 256 * 256;
 }
 
@@ -379,7 +440,7 @@ int sage_gemm_small(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, u
   }
   const int nt = tiles_for(M);
   const size_t lds = lds_for(A.L, nt, A.gs);
-  const unsigned grid = (unsigned)(A.mchunks * A.rt * A.S);
+  const unsigned grid = (unsigned)(A.mchunks * A.rpairs * A.S);
   auto launch = [&](auto kern) {
     static bool attr = false;
     if (!attr) {
@@ -387,11 +448,12 @@ int sage_gemm_small(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, u
                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
       attr = true;
     }
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kGemmThreads), lds, hs, A);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kGThreads), lds, hs, A);
   };
-  if (nt == 1) launch(gemm_kernel<1>);
-  else if (nt == 2) launch(gemm_kernel<2>);
-  else launch(gemm_kernel<4>);
+  if (!A.vec_x) launch(gemm_kernel<1, false>);  // fewer than kPermuteMinRows rows: nt == 1
+  else if (nt == 1) launch(gemm_kernel<1, true>);
+  else if (nt == 2) launch(gemm_kernel<2, true>);
+  else launch(gemm_kernel<4, true>);
   return hip_status();
 }
 
