@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="layer",
-                    choices=["layer", "sweep", "gemm", "moe", "single", "all"])
+                    choices=["layer", "sweep", "gemm", "prefill", "moe", "single", "all"])
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -338,6 +338,11 @@ def bench_single_products(kind, steps, warmup):
             for M in (1, 4, 16, 64):
                 c, X = W.small_batch(shape[0], shape[1], M)
                 cases.append((f"gemm_{shape[0]}x{shape[1]}_M{M}", c, X, M))
+    if kind in ("prefill", "all"):
+        for shape in ((9728, 2560), (2560, 9728)):
+            for M in (128, 256, 512, 1024):
+                c, X = W.small_batch(shape[0], shape[1], M)
+                cases.append((f"prefill_{shape[0]}x{shape[1]}_M{M}", c, X, M))
     for name, c, x, M in cases:
         log(f"[case] {name}")
         base = upload_pack(c)
@@ -457,7 +462,7 @@ def main():
     import bit_vector_quantized_amd as sage
     sage.lib()  # fails loudly when the HIP library is missing
 
-    if args.workload in ("sweep", "gemm", "single", "all"):
+    if args.workload in ("sweep", "gemm", "prefill", "single", "all"):
         bench_single_products(args.workload, args.steps, args.warmup)
     if args.workload in ("moe", "all"):
         bench_moe(args.steps, args.warmup)

@@ -331,6 +331,39 @@ def test_gemm_small_full_size(shape, M):
     check_gemm(f"{shape[0]}x{shape[1]} M={M}", c, X, Y)
 
 
+@pytest.mark.parametrize("M", [128, 200, 512])
+@pytest.mark.parametrize("K,V", [(32, 5), (128, 3)])
+def test_gemm_prefill_shapes(M, K, V):
+    """Prefill-sized batches: several 64-row chunks of activations, ragged last chunk."""
+    import torch
+    rng = W.rng_for(143, M, K)
+    c = W.draw_codes(rng, 130, 1152, K, V)
+    X = W.draw_x(rng, (M, 1152))
+    p = upload_pack(c)
+    Y = sage.gemm_small(p, torch.from_numpy(X).cuda())
+    check_gemm(f"130x1152 K={K} M={M}", c, X, Y)
+
+
+@pytest.mark.parametrize("shape", [(9728, 2560), (2560, 9728)])
+def test_gemm_prefill_full_size_sampled(shape):
+    """M = 1024 at full size, checked on 48 sampled activation rows (first, last and spread)."""
+    import torch
+    c, X = W.small_batch(shape[0], shape[1], 1024)
+    p = upload_pack(c)
+    Y = sage.gemm_small(p, torch.from_numpy(X).cuda())
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 1023], W.rng_for(144).choice(1024, 43, replace=False)]))
+    Wh = decoder.decode(c)
+    Xs = np.asarray(X[rows], np.float64)
+    ref = Xs @ Wh.T
+    got = _np(Y)[rows].astype(np.float64)
+    tol = TOL_REL * np.max(np.abs(Xs) @ np.abs(Wh).T, axis=1)
+    err = np.max(np.abs(got - ref), axis=1)
+    log(f"[gemm] {shape} M=1024 sampled {rows.size} rows: worst err/tol={float(np.max(err / tol)):.3f}")
+    assert np.all(np.isfinite(_np(Y)))
+    assert np.all(err <= tol)
+
+
 def test_gemm_strided_rows():
     import torch
     c = W.draw_codes(W.rng_for(141), 200, 512, 32, 5)
