@@ -74,7 +74,7 @@ def test_gemv_validation(L):
     assert L.sage_gemv(ctypes.byref(_desc()), None, y, None, 0, None) == NULL
     assert L.sage_gemv(ctypes.byref(_desc()), ctypes.c_void_p((1 << 20) + 2), y, None, 0, None) == ALIGN
     # a large matrix needs split-K partials: without a workspace the call is refused
-    big = _desc(d_out=9728, d_in=2560)
+    big = _desc(d_out=2560, d_in=9728)
     n = ctypes.c_size_t(0)
     assert L.sage_gemv_workspace_bytes(ctypes.byref(big), ctypes.byref(n)) == OK
     assert n.value > 0

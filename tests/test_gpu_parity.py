@@ -210,8 +210,8 @@ def test_gemv_split_sweep_full_size(K, V):
 
 def test_gemv_workspace_counters_return_to_zero():
     import torch
-    c = W.draw_codes(W.rng_for(130), 9728, 2560, 64, 4)
-    x = W.draw_x(W.rng_for(131), (2560,))
+    c = W.draw_codes(W.rng_for(130), 2560, 9728, 64, 4)  # wide enough to need split-K
+    x = W.draw_x(W.rng_for(131), (9728,))
     p = upload_pack(c)
     nbytes = sage.gemv_workspace_bytes(p)
     assert nbytes > 0
@@ -221,7 +221,7 @@ def test_gemv_workspace_counters_return_to_zero():
     for _ in range(3):
         outs.append(_np(sage.gemv(p, xd, ws=ws)).copy())
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
-    check_gemv("repeat 9728x2560", c, x, torch.from_numpy(outs[2]).cuda())
+    check_gemv("repeat 2560x9728", c, x, torch.from_numpy(outs[2]).cuda())
 
 
 def test_gemv_zero_input_and_zero_grid():
