@@ -48,6 +48,8 @@ def parse():
                     choices=["layer", "sweep", "gemm", "prefill", "moe", "single", "all"])
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fused", action="store_true",
+                    help="run the SwiGLU block as one sage_mlp launch (3 launches per step)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--eager", action="store_true", help="launch from Python (no graph)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -121,15 +123,18 @@ def load_traffic(name):
 # ------------------------------------------------------------------------------------------------
 
 class LayerBench:
-    ORDER = (("qkv", ("q", "k", "v"), "attn_in"), ("o", ("o",), "attn_out"),
-             ("gateup", ("gate", "up"), "mlp_in"), ("down", ("down",), "mlp_mid"))
-    DOMINANT = "gateup"
+    """The layer step: q|k|v in one launch, o, then the SwiGLU block. Unfused (default): gate|up
+    in one launch and down on the synthetic intermediate vector (two launches). Fused: one
+    sage_mlp launch for gate, up, silu*mul and down."""
+    UNFUSED = (("qkv", ("q", "k", "v"), "attn_in"), ("o", ("o",), "attn_out"),
+               ("gateup", ("gate", "up"), "mlp_in"), ("down", ("down",), "mlp_mid"))
 
-    def __init__(self, copies, steps):
+    def __init__(self, copies, steps, fused=False):
         import torch
         import workloads as W
         import bit_vector_quantized_amd as sage
         self.sage = sage
+        self.fused = fused
         self.layer = W.decoder_layer()
         base = {n: upload_pack(c) for n, c in self.layer.mats.items()}
         self.bytes_per_layer = sum(packed_weight_bytes(p) for p in base.values())
@@ -143,26 +148,57 @@ class LayerBench:
         self.ys = {n: torch.empty(p.d_out, dtype=torch.float16, device="cuda")
                    for n, p in base.items()}
         self.ws = {}
-        for key, names, _ in self.ORDER:
+        for key, names, _ in self.UNFUSED:
             ps = [base[n] for n in names]
             self.ws[key] = sage.workspace(sage.gemv_multi_workspace_bytes(ps), "cuda")
-        self.dom_bytes = sum(algorithmic_bytes(base[n]) for n in ("gate", "up"))
+        self.ws["mlp"] = sage.workspace(
+            sage.mlp_workspace_bytes(base["gate"], base["up"], base["down"]), "cuda")
+        if fused:
+            self.dom_name = "mlp (gate|up 2 x 9728x2560, silu*mul, down 2560x9728 in one launch)"
+            # packed fields, codebooks and permutations of the three matrices, x once, y once
+            self.dom_bytes = sum(algorithmic_bytes(base[n]) - base[n].d_in * 2 - base[n].d_out * 2
+                                 for n in ("gate", "up", "down")) \
+                + base["gate"].d_in * 2 + base["down"].d_out * 2
+            self.launches = 3
+            self.dom_profile = "mlp_qwen3_4b_9728x2560"
+        else:
+            self.dom_name = "gemv_kernel (gate|up, 2 x 9728x2560 in one launch)"
+            self.dom_bytes = sum(algorithmic_bytes(base[n]) for n in ("gate", "up"))
+            self.launches = 4
+            self.dom_profile = "gemv_gateup_9728x2560x2"
         torch.cuda.synchronize()
+
+    def dominant(self, i):
+        mats = self.copies[i % len(self.copies)]
+        if self.fused:
+            self.sage.mlp(mats["gate"], mats["up"], mats["down"], self.xs["mlp_in"],
+                          self.ys["down"], ws=self.ws["mlp"])
+        else:
+            x = self.xs["mlp_in"]
+            self.sage.gemv_multi([mats["gate"], mats["up"]], [x, x],
+                                 [self.ys["gate"], self.ys["up"]], ws=self.ws["gateup"])
 
     def step(self, i, ev=None):
         mats = self.copies[i % len(self.copies)]
-        for key, names, inp in self.ORDER:
+        order = self.UNFUSED[:2] if self.fused else self.UNFUSED
+        for key, names, inp in order:
             ps = [mats[n] for n in names]
             x = self.xs[inp]
-            if ev is not None and key == self.DOMINANT:
+            if ev is not None and key == "gateup":
                 ev[0].record()
             self.sage.gemv_multi(ps, [x] * len(ps), [self.ys[n] for n in names], ws=self.ws[key])
-            if ev is not None and key == self.DOMINANT:
+            if ev is not None and key == "gateup":
+                ev[1].record()
+        if self.fused:
+            if ev is not None:
+                ev[0].record()
+            self.dominant(i)
+            if ev is not None:
                 ev[1].record()
 
 
-def timed_graph(bench, steps, warmup, eager=False):
-    """Returns (wall seconds for `steps` steps, list of dominant-kernel event durations in ms)."""
+def timed_graph(bench, steps, warmup, eager=False, dominant=True):
+    """Returns (wall seconds for `steps` steps, list of dominant-kernel durations in ms)."""
     import torch
     n = len(bench.copies)
     for i in range(warmup):
@@ -207,14 +243,14 @@ def timed_graph(bench, steps, warmup, eager=False):
         g.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    durs = dominant_graph(bench, per, evs)
+    durs = dominant_graph(bench, per, evs) if dominant else []
     return t1 - t0, durs
 
 
 def dominant_graph(bench, count, evs):
-    """Average duration of the dominant launch (gate|up in one launch): a graph of `count` such
-    launches over distinct weight copies, replayed between two HIP events on the stream the
-    kernels run on. The figure includes the short gap between consecutive kernels of a graph."""
+    """Average duration of the dominant launch: a graph of `count` such launches over distinct
+    weight copies, replayed between two HIP events on the stream the kernels run on. The figure
+    includes the short gap between consecutive kernels of a graph."""
     import torch
     del evs
     s = torch.cuda.Stream()
@@ -223,10 +259,7 @@ def dominant_graph(bench, count, evs):
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
             for i in range(count):
-                mats = bench.copies[i % len(bench.copies)]
-                x = bench.xs["mlp_in"]
-                bench.sage.gemv_multi([mats["gate"], mats["up"]], [x, x],
-                                      [bench.ys["gate"], bench.ys["up"]], ws=bench.ws["gateup"])
+                bench.dominant(i)
     torch.cuda.synchronize()
     reps = 10
     with torch.cuda.stream(s):
@@ -478,9 +511,14 @@ def main():
         log("[bench] calibration copy: 268435456 bytes read, 268435456 bytes written")
         del src, dst
     log("[bench] building the decoder layer copies")
-    bench = LayerBench(args.copies, args.steps)
+    bench = LayerBench(args.copies, args.steps, fused=args.fused)
     log(f"[bench] {len(bench.copies)} copies x {bench.bytes_per_layer} packed bytes; "
         f"timing {args.steps} steps after {args.warmup} warmup steps")
+    # the same layer with the SwiGLU block run the other way, for comparison
+    bench.fused = not args.fused
+    alt_wall, _ = timed_graph(bench, args.steps, args.warmup, eager=args.eager, dominant=False)
+    alt_ms = alt_wall * 1e3 / args.steps
+    bench.fused = args.fused
     wall, durs = timed_graph(bench, args.steps, args.warmup, eager=args.eager)
     ms_per_step = wall * 1e3 / args.steps
     value = bench.bytes_per_layer / (ms_per_step * 1e-3) / 1e9
@@ -488,10 +526,10 @@ def main():
     roofline = None
     if dom_ms:
         achieved = bench.dom_bytes / (dom_ms * 1e-3) / 1e9
-        roofline = {"kernel": "gemv_kernel (gate|up, 2 x 9728x2560 in one launch)",
+        roofline = {"kernel": bench.dom_name,
                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": load_traffic("gemv_gateup_9728x2560x2"),
+                    "traffic": load_traffic(bench.dom_profile),
                     "avg_launch_us": round(dom_ms * 1e3, 3),
                     "algorithmic_bytes_per_launch": bench.dom_bytes}
     line = {
@@ -501,9 +539,12 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "fp16 (fp32 accumulate)",
         "data": "synthetic",
         "config": {"workload": "qwen3_4b_decoder_layer_batch1", "split_K_V": [64, 4],
-                   "matrices": 7, "launches_per_step": 4,
+                   "matrices": 7, "launches_per_step": bench.launches,
+                   "swiglu_block": "fused (sage_mlp)" if bench.fused else "two launches",
                    "packed_bytes_per_step": bench.bytes_per_layer,
-                   "weight_copies": len(bench.copies), "timing": "eager" if args.eager else "hip_graph"},
+                   "weight_copies": len(bench.copies), "timing": "eager" if args.eager else "hip_graph",
+                   ("unfused_ms_per_step" if bench.fused else "fused_mlp_ms_per_step"):
+                       round(alt_ms, 5)},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(1e3 / ms_per_step, 1),
         "roofline": roofline,

@@ -66,6 +66,8 @@ _SIGNATURES = {
     "sage_moe_gemv_workspace_bytes": (_I, [_PM, _I, _I, _PSZ]),
     "sage_moe_gemv": (_I, [_PM, _I, _PM, _I, _P, _I, _PP, _PI64, _PP, _PI64, _P, _SZ, _P]),
     "sage_stream_read": (_I, [_P, _SZ, _P, _P]),
+    "sage_mlp_workspace_bytes": (_I, [_PM, _PM, _PM, ctypes.POINTER(ctypes.c_size_t)]),
+    "sage_mlp": (_I, [_PM, _PM, _PM, _P, _P, _P, _P, _SZ, _P]),
 }
 
 
@@ -327,3 +329,26 @@ def stream_read(buf, nbytes: Optional[int] = None, sink=None, stream=None):
         sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
     _check("sage_stream_read", lib().sage_stream_read(_ptr(buf), n, _ptr(sink), _stream(stream)))
     return sink
+
+
+def mlp_workspace_bytes(gate: Packed, up: Packed, down: Packed) -> int:
+    n = ctypes.c_size_t(0)
+    g, u, d = gate.desc(), up.desc(), down.desc()
+    _check("sage_mlp_workspace_bytes", lib().sage_mlp_workspace_bytes(
+        ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), ctypes.byref(n)))
+    return n.value
+
+
+def mlp(gate: Packed, up: Packed, down: Packed, x, y=None, h=None, ws=None, stream=None):
+    """Fused SwiGLU block y = W_down (silu(W_gate x) * (W_up x)) (see sage_mlp in include/sage.h).
+    Pass h (fp16 [inter]) to also receive the intermediate vector."""
+    torch = _torch()
+    _require_cuda(x, y, h, ws)
+    if y is None:
+        y = torch.empty(down.d_out, dtype=torch.float16, device=x.device)
+    if ws is None:
+        ws = workspace(mlp_workspace_bytes(gate, up, down), x.device)
+    g, u, d = gate.desc(), up.desc(), down.desc()
+    _check("sage_mlp", lib().sage_mlp(ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), _ptr(x),
+                                      _ptr(y), _ptr(h), _ptr(ws), ws.numel(), _stream(stream)))
+    return y

@@ -29,6 +29,8 @@
 // Split-K partials go to a caller workspace (coherent stores, no cache-wide fences); the last
 // workgroup of a row-quad (atomic counter) sums them in split order, writes y in fp16 and resets
 // the counter to zero.
+#include <algorithm>
+
 #include "sage_internal.hpp"
 #include "sage_gemv.hpp"
 
@@ -173,7 +175,63 @@ __device__ __forceinline__ float half_dot(const UnitRegs& U, uint32_t h, uint32_
   return acc;
 }
 
-template <int L, bool kWholeX>
+// A producer row group is complete: its fp32 rows are acknowledged, then one signal.
+__device__ inline void signal_row_group(const Job& J, int tid) {
+  wait_stores();
+  __syncthreads();
+  if (tid == 0) counter_add(J.sync);
+}
+
+// Input of a consumer piece (second stage of a fused SwiGLU MLP): waits until every producer row
+// group has signalled, then writes h = fp16(silu(fp16(g)) * fp16(u)) for all d_in entries to xw.
+// The wait is bounded; a wait that runs out is counted in sync[2] and the launch completes.
+constexpr int kSpinLimit = 1 << 17;
+__device__ inline void mlp_input(const Job& J, uint16_t* xw, int tid) {
+  if (tid == 0) {
+    uint32_t n = load_coherent_u32(J.sync);
+    for (int it = 0; n < (uint32_t)J.signal_total && it < kSpinLimit; ++it) {
+      __builtin_amdgcn_s_sleep(8);
+      n = load_coherent_u32(J.sync);
+    }
+    if (n < (uint32_t)J.signal_total) counter_add(J.sync + 2);
+  }
+  __syncthreads();
+  constexpr int kH = kWholeXMax / 4 / kThreads;  // 4-float chunks per thread
+  const uint32_t bytes = (uint32_t)J.d_in * 4u;
+  const __amdgpu_buffer_rsrc_t g_rs = coherent_rsrc(J.src_gate, bytes);
+  const __amdgpu_buffer_rsrc_t u_rs = coherent_rsrc(J.src_up, bytes);
+  u32x4 g[kH], u[kH];
+#pragma unroll
+  for (int i = 0; i < kH; ++i) {
+    const uint32_t off = (uint32_t)(tid + i * kThreads) * 16u;
+    g[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(g_rs, off, 0, 0x10));
+    u[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(u_rs, off, 0, 0x10));
+  }
+  const bool copy_out = J.h_out != nullptr && blockIdx.x == 0;
+#pragma unroll
+  for (int i = 0; i < kH; ++i) {
+    const int e = tid + i * kThreads;
+    if (e * 4 >= J.d_in) continue;
+    uint16_t hv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float g16 = (float)(_Float16)__uint_as_float(g[i][q]);
+      const float u16 = (float)(_Float16)__uint_as_float(u[i][q]);
+      hv[q] = f2h(g16 / (1.0f + __expf(-g16)) * u16);
+    }
+    const uint2 packed = make_uint2(hv[0] | ((uint32_t)hv[1] << 16), hv[2] | ((uint32_t)hv[3] << 16));
+    *reinterpret_cast<uint2*>(xw + e * 4) = packed;
+    if (copy_out) *reinterpret_cast<uint2*>(J.h_out + e * 4) = packed;
+  }
+  if (tid == 0) {
+    if (counter_add(J.sync + 1) == (uint32_t)(J.consumer_wgs - 1)) {
+      counter_reset(J.sync);
+      counter_reset(J.sync + 1);
+    }
+  }
+}
+
+template <int L, bool kWholeX, bool kFused>
 __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int inst, int rq,
                                           int split, uint8_t* smem) {
   using C = SplitC<L>;
@@ -200,8 +258,9 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int i
   // 1. Loads, in the order their data is needed.
   const __amdgpu_buffer_rsrc_t cb_rs = view(R.codebook, C::kK * 16u);
   const __amdgpu_buffer_rsrc_t pi_rs = view(R.pi ? R.pi + c0 : nullptr, R.pi ? cols * 4u : 0u);
+  const bool consumer = kFused && J.src_gate != nullptr;  // input built in LDS from a first stage
   const __amdgpu_buffer_rsrc_t x_rs =
-      view(J.x + (int64_t)inst * J.x_stride, (uint32_t)J.d_in * 2u);
+      view(consumer ? nullptr : J.x + (int64_t)inst * J.x_stride, consumer ? 0u : (uint32_t)J.d_in * 2u);
   const uint8_t* blk0 = R.packed + ((int64_t)(J.tile0 + rt) * J.ng + g0) * kBlockBytes;
   const __amdgpu_buffer_rsrc_t w_rs = view(blk0, tile_ok ? (uint32_t)(ngl * kBlockBytes) : 0u);
 
@@ -245,10 +304,14 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int i
   }
   if constexpr (kWholeX) {
     uint16_t* xw = reinterpret_cast<uint16_t*>(smem + tail + kTailX);
+    if (kFused && consumer) {
+      mlp_input(J, xw, tid);
+    } else {
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i)
-      if (tid + i * kThreads < J.d_in / 8)
-        *reinterpret_cast<u32x4*>(xw + (tid + i * kThreads) * 8) = xc[i];
+      for (int i = 0; i < kChunks; ++i)
+        if (tid + i * kThreads < J.d_in / 8)
+          *reinterpret_cast<u32x4*>(xw + (tid + i * kThreads) * 8) = xc[i];
+    }
     __syncthreads();
     const uint32_t col = (min(src, last) & use_pi) | ((uint32_t)(c0 + tid) & ~use_pi);
     if (tid < cols) xp[tid] = xw[col];
@@ -292,9 +355,13 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int i
   const int row_local = rt * kTileRows + lane;
   const int row = J.tile0 * kTileRows + row_local;
   const bool row_ok = part == 0 && tile_ok && row < J.d_out;
-  uint16_t* y = J.y + (int64_t)inst * J.y_stride;
+  uint16_t* y = J.y != nullptr ? J.y + (int64_t)inst * J.y_stride : nullptr;
   if (J.S == 1) {
-    if (row_ok) y[row] = f2h(acc);
+    if (row_ok) {
+      if (y != nullptr) y[row] = f2h(acc);
+      if (kFused && J.out32 != nullptr) store_coherent(J.out32 + row, acc);
+    }
+    if (kFused && J.out32 != nullptr) signal_row_group(J, tid);
     return;
   }
   float* pbuf = J.partial + (int64_t)inst * J.partial_stride;
@@ -320,12 +387,14 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int i
       for (int q = 0; q < 32; ++q)
         if (sp0 + q < J.S) s += v[q];
     }
-    y[row] = f2h(s);
+    if (y != nullptr) y[row] = f2h(s);
+    if (kFused && J.out32 != nullptr) store_coherent(J.out32 + row, s);
   }
   if (tid == 0) counter_reset(counter);
+  if (kFused && J.out32 != nullptr) signal_row_group(J, tid);
 }
 
-template <bool kWholeX>
+template <bool kWholeX, bool kFused>
 __global__ void __launch_bounds__(kThreads) gemv_kernel(JobTable T) {
   extern __shared__ __align__(16) uint8_t smem[];
   const Job& J = T.jobs[blockIdx.y];
@@ -350,11 +419,11 @@ __global__ void __launch_bounds__(kThreads) gemv_kernel(JobTable T) {
     R.L = J.log2K;
   }
   switch (R.L) {
-    case 4: gemv_body<4, kWholeX>(R, J, inst, rq, split, smem); break;
-    case 5: gemv_body<5, kWholeX>(R, J, inst, rq, split, smem); break;
-    case 6: gemv_body<6, kWholeX>(R, J, inst, rq, split, smem); break;
-    case 7: gemv_body<7, kWholeX>(R, J, inst, rq, split, smem); break;
-    default: gemv_body<8, kWholeX>(R, J, inst, rq, split, smem); break;
+    case 4: gemv_body<4, kWholeX, kFused>(R, J, inst, rq, split, smem); break;
+    case 5: gemv_body<5, kWholeX, kFused>(R, J, inst, rq, split, smem); break;
+    case 6: gemv_body<6, kWholeX, kFused>(R, J, inst, rq, split, smem); break;
+    case 7: gemv_body<7, kWholeX, kFused>(R, J, inst, rq, split, smem); break;
+    default: gemv_body<8, kWholeX, kFused>(R, J, inst, rq, split, smem); break;
   }
 }
 
@@ -511,21 +580,43 @@ int launch(Plan& P, const Job* proto, bool whole, int maxL, void* ws, size_t ws_
   if (need > ws_bytes) return SAGE_ERR_WORKSPACE;
   if (need && !aligned(ws, 256)) return SAGE_ERR_ALIGN;
   if (P.grid_x == 0) return SAGE_OK;
+  // fused stages: producers signal once per row group; consumers wait for all of them
+  int signals = 0, consumers = 0, first_consumer = -1;
+  for (int i = 0; i < P.n; ++i) {
+    const Job& J = T.jobs[i];
+    if (J.out32 != nullptr) signals += J.rq * J.inst;
+    if (J.src_gate != nullptr) {
+      consumers += J.wg_per_inst * J.inst;
+      if (first_consumer < 0) first_consumer = i;
+    }
+  }
+  for (int i = 0; i < P.n; ++i) {
+    Job& J = T.jobs[i];
+    J.signal_total = signals;
+    J.consumer_wgs = consumers;
+    if (i != first_consumer) J.h_out = nullptr;
+  }
+  const bool fused = signals > 0;
+  if (fused && !whole) return SAGE_ERR_ARG;  // the fused block stages its input whole
   static bool attr_done = false;
   if (!attr_done) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_kernel<true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess ||
-        hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_kernel<false>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
-      return SAGE_ERR_HIP;
+    const void* kernels[3] = {reinterpret_cast<const void*>(gemv_kernel<true, false>),
+                              reinterpret_cast<const void*>(gemv_kernel<false, false>),
+                              reinterpret_cast<const void*>(gemv_kernel<true, true>)};
+    for (const void* k : kernels)
+      if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) !=
+          hipSuccess)
+        return SAGE_ERR_HIP;
     attr_done = true;
   }
   const size_t lds = lds_bytes(maxL, gs_max, whole ? d_in_max : 0);
   const dim3 grid((unsigned)P.grid_x, (unsigned)P.n);
-  if (whole)
-    hipLaunchKernelGGL(gemv_kernel<true>, grid, dim3(kThreads), lds, stream, T);
+  if (fused)
+    hipLaunchKernelGGL((gemv_kernel<true, true>), grid, dim3(kThreads), lds, stream, T);
+  else if (whole)
+    hipLaunchKernelGGL((gemv_kernel<true, false>), grid, dim3(kThreads), lds, stream, T);
   else
-    hipLaunchKernelGGL(gemv_kernel<false>, grid, dim3(kThreads), lds, stream, T);
+    hipLaunchKernelGGL((gemv_kernel<false, false>), grid, dim3(kThreads), lds, stream, T);
   return hip_status();
 }
 
@@ -611,6 +702,75 @@ int sage_gemv_multi(const sage_matrix_t* mats, const uint16_t* const* xs, uint16
     whole = whole && whole_x_ok(xs[i], 0, mats[i].d_in);
   }
   return launch(P, proto, whole, maxL, ws, ws_bytes, (hipStream_t)stream);
+}
+
+static int mlp_check(const sage_matrix_t* gate, const sage_matrix_t* up,
+                     const sage_matrix_t* down) {
+  if (gate == nullptr || up == nullptr || down == nullptr) return SAGE_ERR_NULL;
+  int st = check_matrix(gate);
+  if (st == SAGE_OK) st = check_matrix(up);
+  if (st == SAGE_OK) st = check_matrix(down);
+  if (st != SAGE_OK) return st;
+  if (gate->d_out != up->d_out || gate->d_in != up->d_in || down->d_in != gate->d_out)
+    return SAGE_ERR_SHAPE;
+  if (gate->d_in > kWholeXMax || down->d_in > kWholeXMax) return SAGE_ERR_SHAPE;
+  return SAGE_OK;
+}
+
+// Workspace of the fused MLP: split-K partials of all pieces, then gate and up rows in fp32,
+// then the three synchronisation words.
+static size_t mlp_extra_bytes(int inter) { return ((size_t)inter * 8 + 255) / 256 * 256 + 256; }
+
+int sage_mlp_workspace_bytes(const sage_matrix_t* gate, const sage_matrix_t* up,
+                             const sage_matrix_t* down, size_t* bytes) {
+  if (bytes == nullptr) return SAGE_ERR_NULL;
+  int st = mlp_check(gate, up, down);
+  if (st != SAGE_OK) return st;
+  const sage_matrix_t mats[3] = {*gate, *up, *down};
+  Plan P;
+  multi_plan(mats, 3, P);
+  *bytes = plan_workspace(P) + mlp_extra_bytes(gate->d_out);
+  return SAGE_OK;
+}
+
+int sage_mlp(const sage_matrix_t* gate, const sage_matrix_t* up, const sage_matrix_t* down,
+             const uint16_t* x, uint16_t* y, uint16_t* h, void* ws, size_t ws_bytes,
+             sage_stream_t stream) {
+  int st = mlp_check(gate, up, down);
+  if (st != SAGE_OK) return st;
+  if (x == nullptr || y == nullptr || ws == nullptr) return SAGE_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(y, 2) || !aligned(h, 8) || !aligned(ws, 256))
+    return SAGE_ERR_ALIGN;
+  const sage_matrix_t mats[3] = {*gate, *up, *down};
+  Plan P;
+  multi_plan(mats, 3, P);
+  const size_t parts_bytes = plan_workspace(P);
+  if (ws_bytes < parts_bytes + mlp_extra_bytes(gate->d_out)) return SAGE_ERR_WORKSPACE;
+  char* extra = static_cast<char*>(ws) + parts_bytes;
+  float* g32 = reinterpret_cast<float*>(extra);
+  float* u32 = g32 + gate->d_out;
+  uint32_t* sync = reinterpret_cast<uint32_t*>(extra + mlp_extra_bytes(gate->d_out) - 256);
+  Job proto[3];
+  int maxL = 4;
+  for (int i = 0; i < 3; ++i) {
+    Job& J = proto[i];
+    J = Job{};
+    J.packed = static_cast<const uint8_t*>(mats[i].packed);
+    J.codebook = mats[i].codebook;
+    J.pi = mats[i].pi;
+    J.log2K = mats[i].log2K;
+    J.sync = sync;
+    maxL = std::max(maxL, mats[i].log2K);
+  }
+  proto[0].x = x;
+  proto[0].out32 = g32;
+  proto[1].x = x;
+  proto[1].out32 = u32;
+  proto[2].src_gate = g32;
+  proto[2].src_up = u32;
+  proto[2].y = y;
+  proto[2].h_out = h;
+  return launch(P, proto, true, maxL, ws, ws_bytes, (hipStream_t)stream);
 }
 
 int sage_moe_gemv_workspace_bytes(const sage_matrix_t* shapes, int n_mats, int n_sel,

@@ -40,6 +40,18 @@ struct Job {
   int32_t S, gs;            // column splits and groups per split
   int32_t wg_per_inst, inst;
   int32_t counters_stride;
+  // Fused two-stage launches (SwiGLU MLP). A producer piece also writes its rows in fp32 to
+  // out32 with coherent stores and signals sync[0] once per finished row group; a consumer piece
+  // (src_gate set) waits until sync[0] reaches signal_total, then takes its input from
+  // fp16(silu(fp16(gate)) * fp16(up)) of the producers' fp32 rows. sync[1] counts consumers that
+  // passed the wait (the last one resets sync[0..1]); sync[2] counts waits that timed out.
+  float* out32;
+  const float* src_gate;
+  const float* src_up;
+  uint32_t* sync;
+  uint16_t* h_out;          // optional fp16 copy of the consumer input (one workgroup writes it)
+  int32_t signal_total;
+  int32_t consumer_wgs;
 };
 
 // Kernel argument: blockIdx.y selects the piece, blockIdx.x the workgroup inside it.

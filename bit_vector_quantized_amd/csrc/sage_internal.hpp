@@ -118,6 +118,9 @@ __device__ inline __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base, uint32_
 __device__ inline float load_coherent_at(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0x10 /* sc1 */));
 }
+__device__ inline uint32_t load_coherent_u32(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ inline uint32_t counter_add(uint32_t* c) {
   return __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

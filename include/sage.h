@@ -174,6 +174,33 @@ int sage_moe_gemv(const sage_matrix_t* experts_dev, int n_experts, const sage_ma
                   void* ws, size_t ws_bytes, sage_stream_t stream);
 
 /* ------------------------------------------------------------------------------------------
+ * sage_mlp: the SwiGLU feed-forward block of a decoder layer at batch one in one launch,
+ *   y = W_down (silu(W_gate x) * (W_up x)),  silu(t) = t / (1 + exp(-t)),
+ * with W_gate, W_up [inter x hidden] and W_down [hidden_out x inter] SAGE-packed (any splits).
+ * The intermediate follows the unfused sequence of fp16 tensors: gate and up rows are rounded to
+ * fp16, silu and the product are computed in fp32 from those values and rounded to fp16, and that
+ * vector is the input of W_down (gathered through W_down's pi like any other input). The
+ * down-projection workgroups are dispatched after the gate/up ones, issue their weight loads,
+ * then wait (bounded) until every gate/up row group has been written.
+ *   gate, up, down  matrices as for sage_gemv; gate/up same shape, down->d_in == gate->d_out;
+ *                   hidden and inter at most 16384.
+ *   x   fp16 [hidden], original channel order of W_gate/W_up, 16-byte aligned.
+ *   y   fp16 [down->d_out], 2-byte aligned.
+ *   h   optional fp16 [inter] copy of the intermediate (NULL: not written), 8-byte aligned.
+ *   ws  workspace of sage_mlp_workspace_bytes() bytes, 256-byte aligned, zero-filled before its
+ *       first use and left zero-ready by every call (as for sage_gemv). A wait that ran out, which
+ *       needs the down-projection workgroups to be starved for ~0.1 s, is counted in a word of
+ *       ws; results of such a call are undefined and ws must be zero-filled again.
+ * Calls that share a workspace must not overlap. Errors: SAGE_ERR_NULL, _SHAPE (shapes that do
+ * not chain, or wider than 16384), _SPLIT, _ALIGN, _WORKSPACE, _HIP.
+ */
+int sage_mlp_workspace_bytes(const sage_matrix_t* gate, const sage_matrix_t* up,
+                             const sage_matrix_t* down, size_t* bytes);
+int sage_mlp(const sage_matrix_t* gate, const sage_matrix_t* up, const sage_matrix_t* down,
+             const uint16_t* x, uint16_t* y, uint16_t* h, void* ws, size_t ws_bytes,
+             sage_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------
  * sage_stream_read: measurement helper, not part of the decode path. Reads `bytes` bytes at `p`
  * once, in one launch, with the same 16-byte non-temporal buffer loads the decode kernels use for
  * packed weights, and writes nothing unless the data XOR-reduces to a fixed improbable value (then

@@ -10,6 +10,11 @@ Written from "SAGE: Pushing 2-Bit Vector-Quantized LLMs toward Real-World Usabil
   gemv / gemm    y = W_hat x and Y = X W_hat^T in float64 with the fp16 inputs widened exactly.
   moe_gemv       the same product for each routed expert with that expert's own fields.
   tolerance      the output bound used by the parity tests: 2e-3 * max over rows of sum |W_hat||x|.
+  silu, swiglu_mlp
+                 the SwiGLU feed-forward block of the decoder family the paper evaluates (the
+                 paper quantizes these linear layers but does not define the block): the gate and
+                 up products rounded to fp16, h = fp16(silu(gate) * up) with silu(t) = t/(1+e^-t),
+                 then y = W_down h. Only this composition is new here; each product is gemv above.
 
 Every step here is exact in float64: mu, delta and codeword entries are fp16 values, q has at most
 6 bits, so mu + q*delta and its product with a codeword entry need far fewer than 53 bits.
@@ -17,7 +22,8 @@ dequant_fp16 is therefore the correctly rounded fp16 of the exact decoded weight
 
 Parity status: pinned by the CPU tests (exact recovery of planted matrices, the equal-radii special
 case of Appendix A.6, unit-vector probes of the permutation direction and a brute-force loop
-matrix-vector product on tiny shapes).
+matrix-vector product on tiny shapes; silu at closed-form points and the identity
+silu(t) - silu(-t) = t; the block's zero-gate and zero-up cases).
 """
 from __future__ import annotations
 
@@ -111,3 +117,17 @@ def abs_weighted_sum(c: Any, x: np.ndarray) -> np.ndarray:
 def tolerance(c: Any, x: np.ndarray, rel: float = 2e-3) -> float:
     """Bound for max |y - y_ref|: rel * max over rows of sum_c |W_hat_rc| |x_c|."""
     return float(rel * np.max(abs_weighted_sum(c, x)))
+
+
+def silu(t: np.ndarray) -> np.ndarray:
+    """t * sigmoid(t) = t / (1 + exp(-t)) in float64."""
+    t = np.asarray(t, np.float64)
+    return t / (1.0 + np.exp(-t))
+
+
+def swiglu_mlp(gate: Any, up: Any, down: Any, x: np.ndarray):
+    """Returns (h, y): h = fp16(silu(fp16(W_gate x)) * fp16(W_up x)) as float64, y = W_down h."""
+    g16 = gemv(gate, x).astype(np.float16).astype(np.float64)
+    u16 = gemv(up, x).astype(np.float16).astype(np.float64)
+    h = (silu(g16) * u16).astype(np.float16).astype(np.float64)
+    return h, decode(down) @ h

@@ -293,6 +293,74 @@ def test_gemv_multi_sixteen_mixed_products():
         check_gemv(f"mixed[{i}] {c.d_out}x{c.d_in} K={c.K}", c, x, y)
 
 
+# ------------------------------------------------------------------------------ fused SwiGLU block
+
+def _fp16_neighbours(v):
+    """fp16 values one step below, at and above fp16(v) (float64)."""
+    c = np.asarray(v, np.float64).astype(np.float16)
+    lo = np.nextafter(c, np.float16(-np.inf))
+    hi = np.nextafter(c, np.float16(np.inf))
+    return [a.astype(np.float64) for a in (lo, c, hi)]
+
+
+def check_mlp(name, gate, up, down, x, y_dev, h_dev):
+    """h: the kernel rounds its fp32 gate/up sums to fp16, which may land one fp16 step from the
+    rounding of the exact sums, and evaluates silu in fp32; so each h entry must lie within one
+    fp16 ulp of the range of silu(a) * b over a, b in the fp16 neighbours of the exact gate and up
+    values. y: checked against W_down applied to the kernel's own h, with the output tolerance."""
+    import torch
+    torch.cuda.synchronize()
+    g = decoder.gemv(gate, x)
+    u = decoder.gemv(up, x)
+    cands = np.stack([decoder.silu(a) * b for a in _fp16_neighbours(g) for b in _fp16_neighbours(u)])
+    lo, hi = cands.min(axis=0), cands.max(axis=0)
+    h = _np(h_dev).astype(np.float64)
+    ulp = np.spacing(np.maximum(np.abs(lo), np.abs(hi)).astype(np.float16)).astype(np.float64)
+    h_ref, _ = decoder.swiglu_mlp(gate, up, down, x)
+    exact = float(np.mean(h == h_ref))
+    log(f"[mlp] {name}: h equal to the oracle's in {100 * exact:.2f}% of entries")
+    assert np.all(np.isfinite(h))
+    assert np.all((h >= lo - ulp) & (h <= hi + ulp)), name
+    check_gemv(f"{name} (down)", down, h.astype(np.float16), y_dev)
+
+
+@pytest.mark.parametrize("shape", [(256, 384, 128), (512, 1152, 700), (1024, 128, 64)])
+def test_mlp_small(shape):
+    import torch
+    hidden, inter, out = shape
+    rng = W.rng_for(150, *shape)
+    gate = W.draw_codes(rng, inter, hidden, 32, 5)
+    up = W.draw_codes(rng, inter, hidden, 64, 4)
+    down = W.draw_codes(rng, out, inter, 16, 6)
+    x = W.draw_x(rng, (hidden,))
+    pg, pu, pd = upload_pack(gate), upload_pack(up), upload_pack(down)
+    h = torch.empty(inter, dtype=torch.float16, device="cuda")
+    y = sage.mlp(pg, pu, pd, torch.from_numpy(x).cuda(), h=h)
+    check_mlp(f"mlp {hidden}->{inter}->{out}", gate, up, down, x, y, h)
+
+
+def test_mlp_decoder_layer_and_repeat(layer):
+    """The Qwen3-4B-shaped block (9728 x 2560 gate/up, 2560 x 9728 down); three calls on one
+    workspace give the same bits, so the synchronisation words return to zero."""
+    import torch
+    gate, up, down = (layer.mats[n] for n in ("gate", "up", "down"))
+    x = layer.xs[layer.input_of["gate"]]
+    pg, pu, pd = upload_pack(gate), upload_pack(up), upload_pack(down)
+    ws = sage.workspace(sage.mlp_workspace_bytes(pg, pu, pd), "cuda")
+    xd = torch.from_numpy(x).cuda()
+    h = torch.empty(gate.d_out, dtype=torch.float16, device="cuda")
+    outs = []
+    for i in range(3):
+        y = sage.mlp(pg, pu, pd, xd, h=h if i == 0 else None, ws=ws)
+        torch.cuda.synchronize()
+        outs.append(_np(y).copy())
+        if i == 0:
+            check_mlp("layer mlp", gate, up, down, x, y, h)
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+    sync = _np(ws.view(torch.int32)[-64:])
+    assert np.all(sync == 0), "synchronisation words must return to zero (no timed-out waits)"
+
+
 # ------------------------------------------------------------------------------ small-batch gemm
 
 def check_gemm(name, c, X, Y_dev, W_hat=None):

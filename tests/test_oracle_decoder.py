@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 from oracle import budget, decoder
-from workloads import draw_codes, rng_for
+from workloads import draw_codes, draw_x, rng_for
 
 
 def _fp16_bits(a):
@@ -172,3 +172,48 @@ def test_storage_figures_from_the_paper():
     assert budget.codebook_bytes(64) == 1024
     assert budget.payload_bytes(9728, 2560, 64, 4) == 9728 * 2560 * 18 / 64
     assert budget.grid_bytes(9728, 2560) == 9728 * 20 * 4
+
+
+# ------------------------------------------------------------------------------ SwiGLU block
+
+def test_silu_closed_forms():
+    e = np.e
+    assert decoder.silu(0.0) == 0.0
+    assert abs(decoder.silu(1.0) - 1.0 / (1.0 + 1.0 / e)) < 1e-15
+    assert abs(decoder.silu(-1.0) - (-1.0) / (1.0 + e)) < 1e-15
+    assert abs(decoder.silu(2.0) - 2.0 * e * e / (1.0 + e * e)) < 1e-15
+    assert abs(decoder.silu(40.0) - 40.0) < 1e-12 and abs(decoder.silu(-40.0)) < 1e-15
+    t = np.random.default_rng(7).normal(0, 3, 1000)
+    assert np.allclose(decoder.silu(t) - decoder.silu(-t), t, rtol=0, atol=1e-12)
+
+
+def _mlp_codes(seed, hidden=256, inter=384, out=128):
+    rng = rng_for(seed)
+    gate = draw_codes(rng, inter, hidden, 32, 5)
+    up = draw_codes(rng, inter, hidden, 64, 4)
+    down = draw_codes(rng, out, inter, 16, 6)
+    x = draw_x(rng, (hidden,))
+    return gate, up, down, x
+
+
+def test_swiglu_zero_gate_or_up_gives_zero():
+    for which in ("gate", "up"):
+        gate, up, down, x = _mlp_codes(901)
+        c = gate if which == "gate" else up
+        c.mu[:] = 0
+        c.delta[:] = 0
+        h, y = decoder.swiglu_mlp(gate, up, down, x)
+        assert np.all(h == 0) and np.all(y == 0), which
+
+
+def test_swiglu_intermediate_is_fp16_and_follows_gate_sign():
+    gate, up, down, x = _mlp_codes(902)
+    h, y = decoder.swiglu_mlp(gate, up, down, x)
+    assert np.array_equal(h, h.astype(np.float16).astype(np.float64))
+    g = decoder.gemv(gate, x)
+    u = decoder.gemv(up, x)
+    # silu(t) = t * sigmoid(t) keeps the sign of t, so h has the sign of g * u
+    big = (np.abs(g) > 0.5) & (np.abs(u) > 0.05)
+    assert big.sum() > 10
+    assert np.all(np.sign(h[big]) == np.sign(g[big]) * np.sign(u[big]))
+    assert y.shape == (down.d_out,)
