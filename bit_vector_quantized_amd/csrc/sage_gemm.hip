@@ -28,6 +28,7 @@ constexpr int kGMaxGS = 8;                           // column groups per split
 constexpr int kGMaxUnits = kGMaxGS / kGParts;        // groups per wavefront
 constexpr int kPermuteMinRows = 8;                   // from this many rows on, X is permuted once
 constexpr int kDirectRows = kPermuteMinRows;         // rows gathered straight from X below that
+constexpr int kPrefillMinRows = 128;                 // prefill kernel candidates from this many rows
 constexpr uint32_t kNowhere = 1u << 30;              // an offset past every range
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -326,6 +327,225 @@ __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs A) {
   }
 }
 
+// ------------------------------------------------------------------------------------------------
+// Prefill-sized batches (SAGE paper §3.5 / Fig. 6b: decode each weight once per output tile and
+// reuse it across many activation rows). A wavefront owns one 64-row weight tile and 128
+// activation rows, as 2 x 4 tiles of v_mfma_f32_32x32x16_f16 (128 fp32 accumulators per lane).
+// In the B operand lane l supplies weight row l % 32 of a 32-row subtile and channels
+// 8 (l / 32) .. +7 of the 16-channel step, i.e. one subvector: step s of a group uses subvectors
+// 2s (lanes 0-31) and 2s + 1 (lanes 32-63). A workgroup (4 waves, 4 weight tiles) shares a
+// double-buffered activation slab [128 rows][128 channels] in LDS; the loop over column groups
+// prefetches the next group's packed words and activations into registers while the current
+// group runs, so every weight is decoded once per 128 activation rows.
+constexpr int kPfWaves = 4;
+constexpr int kPfThreads = kPfWaves * 64;
+constexpr int kPfRows = 128;                          // activation rows per workgroup
+constexpr int kPfStride = kGroupCols + 8;             // fp16 per staged activation row (padded)
+constexpr int kPfSlab = kPfRows * kPfStride * 2;      // bytes per slab buffer
+constexpr int kPfChunks = kPfRows * kGroupCols / 8 / kPfThreads;  // 16-byte chunks per thread
+
+typedef float float16_t __attribute__((ext_vector_type(16)));
+
+struct PrefillArgs {
+  const uint8_t* packed;
+  const uint16_t* codebook;
+  const uint16_t* Xp;   // activations in permuted order, [M][d_in]
+  uint16_t* Y;
+  int64_t ldy;
+  int32_t d_out, d_in, M, L;
+  int32_t rt, ng;
+};
+
+__host__ __device__ inline uint32_t prefill_slab_offset(int L) {
+  return (1u << L) * 256u + 256u;  // after the codebook replicas and the sign-mask table
+}
+
+// One lane's packed words of one row in one group: payload dwords P0..P7, then X and G.
+struct RowWords {
+  u32x4 a, b;
+  u32x2 side;
+};
+
+template <int L>
+__device__ __forceinline__ half8_t decode_b(uint32_t P, uint32_t X, uint32_t G, int s, int h,
+                                            const uint8_t* cb, const uint2* smask,
+                                            uint32_t laneoff) {
+  constexpr uint32_t kK = 1u << L;
+  // subvector 2s + h of the group: pair s, half a (h = 0) or b (h = 1)
+  const uint32_t f = (P >> (h ? 18 : 8)) & 1023u;
+  const uint32_t lo = h ? (P & 15u) : ((P >> 4) & 15u);
+  const uint32_t hi = h ? ((X >> (4 * s)) & 15u) : (P >> 28);
+  const float mu = h2f(G);
+  const float dl = h2f(G >> 16);
+  const float r = fmaf((float)(f >> L), dl, mu);
+  const _Float16 rh = (_Float16)r;
+  const half2_t r2 = half2_t{rh, rh};
+  const uint4 c = *reinterpret_cast<const uint4*>(cb + (f & (kK - 1u)) * 256 + laneoff);
+  const uint2 mlo = smask[lo];
+  const uint2 mhi = smask[hi];
+  return __builtin_bit_cast(
+      half8_t, make_uint4(mul_pair(c.x ^ mlo.x, r2), mul_pair(c.y ^ mlo.y, r2),
+                          mul_pair(c.z ^ mhi.x, r2), mul_pair(c.w ^ mhi.y, r2)));
+}
+
+template <int L>
+__device__ void prefill_body(const PrefillArgs& A, uint8_t* smem) {
+  constexpr uint32_t kK = 1u << L;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int h = lane >> 5;                    // k half of the 16-channel step
+  const int r0 = lane & 31;                   // rows r0 and 32 + r0 of the tile
+  const int rt = blockIdx.x * kPfWaves + wave;
+  const bool tile_ok = rt < A.rt;
+  const int m0 = blockIdx.y * kPfRows;
+  const int mrows = min(A.M - m0, kPfRows);
+  const int ng = A.ng;
+  uint8_t* cb = smem;
+  uint2* smask = reinterpret_cast<uint2*>(smem + kK * 256);
+  _Float16* slab0 = reinterpret_cast<_Float16*>(smem + prefill_slab_offset(L));
+
+  const __amdgpu_buffer_rsrc_t cb_rs = view(A.codebook, kK * 16u);
+  const __amdgpu_buffer_rsrc_t w_rs =
+      view(A.packed + (int64_t)rt * ng * kBlockBytes, tile_ok ? (uint32_t)(ng * kBlockBytes) : 0u);
+  const __amdgpu_buffer_rsrc_t x_rs =
+      view(A.Xp + (int64_t)m0 * A.d_in, (uint32_t)(mrows * A.d_in * 2));
+  // per-lane byte offsets, fixed for the whole loop; the group adds a uniform amount
+  const uint32_t wa0 = kPlaneA + r0 * 16, wb0 = kPlaneB + r0 * 16, ws0 = kSidePlane + r0 * 8;
+  uint32_t xo[kPfChunks], so[kPfChunks];
+#pragma unroll
+  for (int i = 0; i < kPfChunks; ++i) {
+    const int e = tid + i * kPfThreads;
+    const int m = e >> 4, ch = e & 15;  // 16 chunks of 8 channels per row
+    xo[i] = (uint32_t)((m * A.d_in + ch * 8) * 2);
+    so[i] = (uint32_t)((m * kPfStride + ch * 8) * 2);
+  }
+
+  const u32x4 cw = __builtin_amdgcn_raw_buffer_load_b128(cb_rs, tid * 16, 0, 0);
+  // Packed words run two groups ahead through a three-deep register ring (group g computes from
+  // slot g % 3; no slot is copied, so no wait covers a later group). Activations run one group
+  // ahead (they come from L2): loaded at the start of a group, staged in LDS at its end, and
+  // issued before the packed words so that waiting for them does not wait for the words.
+  RowWords wr[3][2];
+  u32x4 xr[kPfChunks];
+#define SAGE_PF_WORDS(slot, grp)                                                              \
+  {                                                                                          \
+    const uint32_t wg_ = (grp) < ng ? (uint32_t)(grp) * kBlockBytes : kNowhere;              \
+    _Pragma("unroll") for (int t = 0; t < 2; ++t) {                                          \
+      wr[slot][t].a = __builtin_amdgcn_raw_buffer_load_b128(w_rs, wg_ + wa0 + t * 512, 0, 2); \
+      wr[slot][t].b = __builtin_amdgcn_raw_buffer_load_b128(w_rs, wg_ + wb0 + t * 512, 0, 2); \
+      wr[slot][t].side = __builtin_amdgcn_raw_buffer_load_b64(w_rs, wg_ + ws0 + t * 256, 0, 2); \
+    }                                                                                        \
+  }
+#define SAGE_PF_X(grp)                                                                       \
+  {                                                                                          \
+    const uint32_t xg_ = (grp) < ng ? (uint32_t)(grp) * (kGroupCols * 2) : kNowhere;         \
+    _Pragma("unroll") for (int i = 0; i < kPfChunks; ++i)                                    \
+      xr[i] = __builtin_amdgcn_raw_buffer_load_b128(x_rs, xg_ + xo[i], 0, 0);                \
+  }
+#define SAGE_PF_STAGE(buf)                                                                   \
+  _Pragma("unroll") for (int i = 0; i < kPfChunks; ++i)                                      \
+    *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(slab0) + (buf) * kPfSlab + so[i]) = \
+        xr[i];
+  SAGE_PF_X(0)
+  SAGE_PF_WORDS(0, 0)
+  SAGE_PF_WORDS(1, 1)
+  if (tid < (int)kK) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) *reinterpret_cast<u32x4*>(cb + tid * 256 + r * 16) = cw;
+  }
+  if (tid < 16) smask[tid] = nibble_masks((uint32_t)tid);
+  SAGE_PF_STAGE(0)
+  __syncthreads();
+
+  float16_t acc[2][4];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[t][q][v] = 0.0f;
+  const uint32_t laneoff = (uint32_t)(lane & 15) * 16u;
+
+  // one group: activations of g + 1 and words of g + 2 (slot (k + 2) % 3) in flight, multiply
+  // group g (slot k, LDS buffer g & 1), stage g + 1 into the other buffer
+#define SAGE_PF_GROUP(k)                                                                      \
+  {                                                                                           \
+    const int gg = g + (k);                                                                   \
+    SAGE_PF_X(gg + 1)                                                                         \
+    SAGE_PF_WORDS(((k) + 2) % 3, gg + 2)                                                      \
+    const uint8_t* slab = reinterpret_cast<const uint8_t*>(slab0) + (gg & 1) * kPfSlab;       \
+    _Pragma("unroll") for (int s = 0; s < 8; ++s) {                                           \
+      half8_t b[2];                                                                           \
+      _Pragma("unroll") for (int t = 0; t < 2; ++t) {                                         \
+        const uint32_t P = s < 4 ? wr[k][t].a[s] : wr[k][t].b[s - 4];                         \
+        b[t] = decode_b<L>(P, wr[k][t].side[0], wr[k][t].side[1], s, h, cb, smask, laneoff);  \
+      }                                                                                       \
+      _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                         \
+        const half8_t a = *reinterpret_cast<const half8_t*>(                                  \
+            slab + ((q * 32 + r0) * kPfStride + s * 16 + 8 * h) * 2);                         \
+        _Pragma("unroll") for (int t = 0; t < 2; ++t)                                         \
+          acc[t][q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b[t], acc[t][q], 0, 0, 0);    \
+      }                                                                                       \
+      __builtin_amdgcn_sched_barrier(0);                                                      \
+    }                                                                                         \
+    SAGE_PF_STAGE((gg + 1) & 1)                                                               \
+    __syncthreads();                                                                          \
+  }
+  // the group count is rounded up to a multiple of three: groups past the last read zeros
+  // (out-of-range loads) and add nothing, which keeps the loop free of exits that would
+  // multiply the register ring
+  for (int g = 0; g < ng; g += 3) {
+    SAGE_PF_GROUP(0)
+    SAGE_PF_GROUP(1)
+    SAGE_PF_GROUP(2)
+  }
+#undef SAGE_PF_GROUP
+#undef SAGE_PF_STAGE
+#undef SAGE_PF_X
+#undef SAGE_PF_WORDS
+
+  // D layout: lane holds weight row l % 32 of each subtile and activation rows
+  // 8 (v / 4) + 4 (l / 32) + v % 4 of each 32-row block.
+  if (!tile_ok) return;
+  const __amdgpu_buffer_rsrc_t y_rs =
+      view(A.Y + (int64_t)m0 * A.ldy, (uint32_t)((int64_t)mrows * A.ldy * 2));
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int n = rt * kTileRows + t * 32 + r0;
+    if (n >= A.d_out) continue;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = q * 32 + 8 * (v / 4) + 4 * h + (v % 4);
+        // rows past mrows fall outside y_rs and are dropped
+        __builtin_amdgcn_raw_buffer_store_b16(f2h(acc[t][q][v]), y_rs,
+                                              (uint32_t)((m * (int)A.ldy + n) * 2), 0, 0);
+      }
+  }
+}
+
+__global__ void __launch_bounds__(kPfThreads) prefill_kernel(PrefillArgs A) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  switch (A.L) {
+    case 4: prefill_body<4>(A, smem); break;
+    case 5: prefill_body<5>(A, smem); break;
+    case 6: prefill_body<6>(A, smem); break;
+    case 7: prefill_body<7>(A, smem); break;
+    default: prefill_body<8>(A, smem); break;
+  }
+}
+
+// The prefill kernel keeps one wave per SIMD busy for a whole column loop, so it pays off only
+// when its grid covers at least half the compute units; otherwise the small-batch kernel's
+// split-K spreads the same work wider (measured on 9728x2560 and 2560x9728, M = 128 ... 1024).
+bool use_prefill(int d_out, int M) {
+  if (M < kPrefillMinRows) return false;
+  const int64_t wgs = (int64_t)ceil_div(ceil_div(d_out, kTileRows), kPfWaves) * ceil_div(M, kPfRows);
+  return 2 * wgs >= device_cu_count();
+}
+
 int tiles_for(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
 
 constexpr size_t kLdsLimit = 160 * 1024;
@@ -362,7 +582,7 @@ size_t permuted_bytes(int M, int d_in) {
 
 size_t workspace_for(const GemmArgs& A) {
   const size_t xp = permuted_bytes(A.M, A.d_in);
-  if (A.S == 1) return xp;
+  if (use_prefill(A.d_out, A.M) || A.S == 1) return xp;
   const size_t part = (size_t)A.mchunks * A.S * A.mrows_chunk * A.rt * kTileRows * 4;
   const size_t cnt = (size_t)A.mchunks * A.rpairs * 4;
   return xp + (part + cnt + 255) / 256 * 256;
@@ -431,6 +651,30 @@ int sage_gemm_small(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, u
     const int64_t n = (int64_t)M * A.d_in;
     hipLaunchKernelGGL(permute_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, hs,
                        X, (int64_t)ldx, m->pi, A.d_in, M, Xp);
+    if (use_prefill(A.d_out, M)) {
+      PrefillArgs P{};
+      P.packed = A.packed;
+      P.codebook = A.codebook;
+      P.Xp = Xp;
+      P.Y = Y;
+      P.ldy = ldy;
+      P.d_out = A.d_out;
+      P.d_in = A.d_in;
+      P.M = M;
+      P.L = A.L;
+      P.rt = A.rt;
+      P.ng = A.ng;
+      static bool pf_attr = false;
+      if (!pf_attr) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        pf_attr = true;
+      }
+      const dim3 grid((unsigned)ceil_div(A.rt, kPfWaves), (unsigned)ceil_div(M, kPfRows));
+      const size_t lds = prefill_slab_offset(A.L) + 2 * (size_t)kPfSlab;
+      hipLaunchKernelGGL(prefill_kernel, grid, dim3(kPfThreads), lds, hs, P);
+      return hip_status();
+    }
     A.X = Xp;
     A.ldx = A.d_in;
     A.pi = nullptr;

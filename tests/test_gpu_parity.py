@@ -432,6 +432,30 @@ def test_gemm_prefill_full_size_sampled(shape):
     assert np.all(err <= tol)
 
 
+@pytest.mark.parametrize("d_out,d_in,M,K,V", [(4096, 1152, 1000, 64, 4), (4000, 640, 1030, 256, 2),
+                                               (8192, 384, 520, 16, 6)])
+def test_gemm_prefill_kernel(d_out, d_in, M, K, V):
+    """Grids wide enough for the prefill kernel (ragged weight tiles, ragged 128-row blocks, one to
+    nine column groups); checked on 64 sampled activation rows."""
+    import torch
+    rng = W.rng_for(145, d_out, d_in, M)
+    c = W.draw_codes(rng, d_out, d_in, K, V)
+    X = W.draw_x(rng, (M, d_in))
+    p = upload_pack(c)
+    Y = sage.gemm_small(p, torch.from_numpy(X).cuda())
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 127, 128, M - 1], rng.choice(M, 60, replace=False)]))
+    Wh = decoder.decode(c)
+    Xs = np.asarray(X[rows], np.float64)
+    ref = Xs @ Wh.T
+    got = _np(Y)[rows].astype(np.float64)
+    tol = TOL_REL * np.max(np.abs(Xs) @ np.abs(Wh).T, axis=1)
+    err = np.max(np.abs(got - ref), axis=1)
+    log(f"[gemm] prefill {d_out}x{d_in} M={M} K={K}: worst err/tol={float(np.max(err / tol)):.3f}")
+    assert np.all(np.isfinite(_np(Y)))
+    assert np.all(err <= tol)
+
+
 def test_gemm_strided_rows():
     import torch
     c = W.draw_codes(W.rng_for(141), 200, 512, 32, 5)
