@@ -107,9 +107,6 @@ __device__ inline const __attribute__((address_space(1))) T* gview(const T* p) {
 __device__ inline void store_coherent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ inline float load_coherent(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ inline void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Coherent (sc1) loads through a buffer descriptor: unlike atomic loads they can be batched.
 __device__ inline __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base, uint32_t bytes) {

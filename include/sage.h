@@ -141,8 +141,11 @@ int sage_gemv_multi(const sage_matrix_t* mats, const uint16_t* const* xs, uint16
  * §3.5 and App. A.1, where each decoded weight is reused across the rows).
  *   X   fp16 [M][ldx] row-major, original channel order, ldx >= d_in, ldx even, 4-byte aligned.
  *   Y   fp16 [M][ldy] row-major, ldy >= d_out.
- *   M   >= 1. Any M is accepted; the kernels are tuned for M <= 64.
- *   ws  as for sage_gemv, size from sage_gemm_small_workspace_bytes().
+ *   M   >= 1. M = 1 runs the batch-one kernel; up to a few hundred rows a small-batch kernel
+ *       (one decode feeds 16-64 rows); prefill-sized batches whose grid fills the device run a
+ *       kernel that decodes each weight once per 128 rows and loops over all column groups.
+ *   ws  as for sage_gemv, size from sage_gemm_small_workspace_bytes(); from 8 rows on it also
+ *       holds X in permuted column order (written by the call).
  */
 int sage_gemm_small_workspace_bytes(const sage_matrix_t* m, int M, size_t* bytes);
 int sage_gemm_small(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, uint16_t* Y,
