@@ -339,10 +339,13 @@ __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs A) {
 // group runs, so every weight is decoded once per 128 activation rows.
 constexpr int kPfWaves = 4;
 constexpr int kPfThreads = kPfWaves * 64;
-constexpr int kPfRows = 128;                          // activation rows per workgroup
 constexpr int kPfStride = kGroupCols + 8;             // fp16 per staged activation row (padded)
-constexpr int kPfSlab = kPfRows * kPfStride * 2;      // bytes per slab buffer
-constexpr int kPfChunks = kPfRows * kGroupCols / 8 / kPfThreads;  // 16-byte chunks per thread
+// kQ 32-row blocks of activations per workgroup (4 or 8): rows, slab bytes, 16-byte chunks/thread
+template <int kQ> struct PfShape {
+  static constexpr int kRows = 32 * kQ;
+  static constexpr int kSlab = kRows * kPfStride * 2;
+  static constexpr int kChunks = kRows * kGroupCols / 8 / kPfThreads;
+};
 
 typedef float float16_t __attribute__((ext_vector_type(16)));
 
@@ -388,9 +391,12 @@ __device__ __forceinline__ half8_t decode_b(uint32_t P, uint32_t X, uint32_t G, 
                           mul_pair(c.z ^ mhi.x, r2), mul_pair(c.w ^ mhi.y, r2)));
 }
 
-template <int L>
+template <int L, int kQ>
 __device__ void prefill_body(const PrefillArgs& A, uint8_t* smem) {
   constexpr uint32_t kK = 1u << L;
+  constexpr int kPfRows = PfShape<kQ>::kRows;
+  constexpr int kPfSlab = PfShape<kQ>::kSlab;
+  constexpr int kPfChunks = PfShape<kQ>::kChunks;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -412,14 +418,11 @@ __device__ void prefill_body(const PrefillArgs& A, uint8_t* smem) {
       view(A.Xp + (int64_t)m0 * A.d_in, (uint32_t)(mrows * A.d_in * 2));
   // per-lane byte offsets, fixed for the whole loop; the group adds a uniform amount
   const uint32_t wa0 = kPlaneA + r0 * 16, wb0 = kPlaneB + r0 * 16, ws0 = kSidePlane + r0 * 8;
-  uint32_t xo[kPfChunks], so[kPfChunks];
-#pragma unroll
-  for (int i = 0; i < kPfChunks; ++i) {
-    const int e = tid + i * kPfThreads;
-    const int m = e >> 4, ch = e & 15;  // 16 chunks of 8 channels per row
-    xo[i] = (uint32_t)((m * A.d_in + ch * 8) * 2);
-    so[i] = (uint32_t)((m * kPfStride + ch * 8) * 2);
-  }
+  // chunk i of a thread: activation row (tid / 16) + 16 i, channels 8 (tid % 16) .. +7
+  const uint32_t xbase = (uint32_t)(((tid >> 4) * A.d_in + (tid & 15) * 8) * 2);
+  const uint32_t xstep = (uint32_t)(16 * A.d_in * 2);
+  const uint32_t sbase = (uint32_t)(((tid >> 4) * kPfStride + (tid & 15) * 8) * 2);
+  constexpr uint32_t kSStep = 16 * kPfStride * 2;
 
   const u32x4 cw = __builtin_amdgcn_raw_buffer_load_b128(cb_rs, tid * 16, 0, 0);
   // Packed words run two groups ahead through a three-deep register ring (group g computes from
@@ -441,12 +444,12 @@ __device__ void prefill_body(const PrefillArgs& A, uint8_t* smem) {
   {                                                                                          \
     const uint32_t xg_ = (grp) < ng ? (uint32_t)(grp) * (kGroupCols * 2) : kNowhere;         \
     _Pragma("unroll") for (int i = 0; i < kPfChunks; ++i)                                    \
-      xr[i] = __builtin_amdgcn_raw_buffer_load_b128(x_rs, xg_ + xo[i], 0, 0);                \
+      xr[i] = __builtin_amdgcn_raw_buffer_load_b128(x_rs, xg_ + xbase + i * xstep, 0, 0);    \
   }
 #define SAGE_PF_STAGE(buf)                                                                   \
   _Pragma("unroll") for (int i = 0; i < kPfChunks; ++i)                                      \
-    *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(slab0) + (buf) * kPfSlab + so[i]) = \
-        xr[i];
+    *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(slab0) + (buf) * kPfSlab + sbase +  \
+                              i * kSStep) = xr[i];
   SAGE_PF_X(0)
   SAGE_PF_WORDS(0, 0)
   SAGE_PF_WORDS(1, 1)
@@ -458,11 +461,11 @@ __device__ void prefill_body(const PrefillArgs& A, uint8_t* smem) {
   SAGE_PF_STAGE(0)
   __syncthreads();
 
-  float16_t acc[2][4];
+  float16_t acc[2][kQ];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < kQ; ++q)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[t][q][v] = 0.0f;
   const uint32_t laneoff = (uint32_t)(lane & 15) * 16u;
@@ -481,7 +484,7 @@ __device__ void prefill_body(const PrefillArgs& A, uint8_t* smem) {
         const uint32_t P = s < 4 ? wr[k][t].a[s] : wr[k][t].b[s - 4];                         \
         b[t] = decode_b<L>(P, wr[k][t].side[0], wr[k][t].side[1], s, h, cb, smask, laneoff);  \
       }                                                                                       \
-      _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                         \
+      _Pragma("unroll") for (int q = 0; q < kQ; ++q) {                                        \
         const half8_t a = *reinterpret_cast<const half8_t*>(                                  \
             slab + ((q * 32 + r0) * kPfStride + s * 16 + 8 * h) * 2);                         \
         _Pragma("unroll") for (int t = 0; t < 2; ++t)                                         \
@@ -515,7 +518,7 @@ __device__ void prefill_body(const PrefillArgs& A, uint8_t* smem) {
     const int n = rt * kTileRows + t * 32 + r0;
     if (n >= A.d_out) continue;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < kQ; ++q)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int m = q * 32 + 8 * (v / 4) + 4 * h + (v % 4);
@@ -526,15 +529,26 @@ __device__ void prefill_body(const PrefillArgs& A, uint8_t* smem) {
   }
 }
 
+template <int kQ>
 __global__ void __launch_bounds__(kPfThreads) prefill_kernel(PrefillArgs A) {
   extern __shared__ __align__(16) uint8_t smem[];
   switch (A.L) {
-    case 4: prefill_body<4>(A, smem); break;
-    case 5: prefill_body<5>(A, smem); break;
-    case 6: prefill_body<6>(A, smem); break;
-    case 7: prefill_body<7>(A, smem); break;
-    default: prefill_body<8>(A, smem); break;
+    case 4: prefill_body<4, kQ>(A, smem); break;
+    case 5: prefill_body<5, kQ>(A, smem); break;
+    case 6: prefill_body<6, kQ>(A, smem); break;
+    case 7: prefill_body<7, kQ>(A, smem); break;
+    default: prefill_body<8, kQ>(A, smem); break;
   }
+}
+
+// Activation blocks per workgroup: 8 (each decoded subvector feeds 8 MFMAs) when two 256-row slabs
+// fit next to the codebook and the grid of 256-row workgroups still covers half the compute
+// units; else 4 (measured: 9728x2560 at M = 1024 runs 105 us with 8, 123 us with 4; at M = 512
+// the 8-block grid is too small and takes 98 us against 70 us).
+int prefill_blocks(int L, int rt, int M) {
+  const size_t lds8 = prefill_slab_offset(L) + 2 * (size_t)PfShape<8>::kSlab;
+  const int64_t wgs8 = (int64_t)ceil_div(rt, kPfWaves) * ceil_div(M, PfShape<8>::kRows);
+  return (lds8 <= 160 * 1024 && 2 * wgs8 >= device_cu_count()) ? 8 : 4;
 }
 
 // The prefill kernel keeps one wave per SIMD busy for a whole column loop, so it pays off only
@@ -542,7 +556,7 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(PrefillArgs A) {
 // split-K spreads the same work wider (measured on 9728x2560 and 2560x9728, M = 128 ... 1024).
 bool use_prefill(int d_out, int M) {
   if (M < kPrefillMinRows) return false;
-  const int64_t wgs = (int64_t)ceil_div(ceil_div(d_out, kTileRows), kPfWaves) * ceil_div(M, kPfRows);
+  const int64_t wgs = (int64_t)ceil_div(ceil_div(d_out, kTileRows), kPfWaves) * ceil_div(M, 128);
   return 2 * wgs >= device_cu_count();
 }
 
@@ -666,13 +680,21 @@ int sage_gemm_small(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, u
       P.ng = A.ng;
       static bool pf_attr = false;
       if (!pf_attr) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<4>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<8>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         pf_attr = true;
       }
-      const dim3 grid((unsigned)ceil_div(A.rt, kPfWaves), (unsigned)ceil_div(M, kPfRows));
-      const size_t lds = prefill_slab_offset(A.L) + 2 * (size_t)kPfSlab;
-      hipLaunchKernelGGL(prefill_kernel, grid, dim3(kPfThreads), lds, hs, P);
+      if (prefill_blocks(A.L, A.rt, M) == 8) {
+        const dim3 grid((unsigned)ceil_div(A.rt, kPfWaves), (unsigned)ceil_div(M, PfShape<8>::kRows));
+        const size_t lds = prefill_slab_offset(A.L) + 2 * (size_t)PfShape<8>::kSlab;
+        hipLaunchKernelGGL(prefill_kernel<8>, grid, dim3(kPfThreads), lds, hs, P);
+      } else {
+        const dim3 grid((unsigned)ceil_div(A.rt, kPfWaves), (unsigned)ceil_div(M, PfShape<4>::kRows));
+        const size_t lds = prefill_slab_offset(A.L) + 2 * (size_t)PfShape<4>::kSlab;
+        hipLaunchKernelGGL(prefill_kernel<4>, grid, dim3(kPfThreads), lds, hs, P);
+      }
       return hip_status();
     }
     A.X = Xp;

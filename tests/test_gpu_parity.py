@@ -433,10 +433,12 @@ def test_gemm_prefill_full_size_sampled(shape):
 
 
 @pytest.mark.parametrize("d_out,d_in,M,K,V", [(4096, 1152, 1000, 64, 4), (4000, 640, 1030, 256, 2),
-                                               (8192, 384, 520, 16, 6)])
+                                               (8192, 384, 520, 16, 6), (8192, 384, 1100, 16, 6),
+                                               (8000, 640, 1030, 64, 4)])
 def test_gemm_prefill_kernel(d_out, d_in, M, K, V):
-    """Grids wide enough for the prefill kernel (ragged weight tiles, ragged 128-row blocks, one to
-    nine column groups); checked on 64 sampled activation rows."""
+    """Grids wide enough for the prefill kernel, with 128-row and (last two) 256-row activation
+    blocks: ragged weight tiles, ragged last block, three to nine column groups; checked on 64
+    sampled activation rows."""
     import torch
     rng = W.rng_for(145, d_out, d_in, M)
     c = W.draw_codes(rng, d_out, d_in, K, V)
