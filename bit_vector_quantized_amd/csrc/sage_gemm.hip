@@ -354,9 +354,11 @@ struct PrefillArgs {
   const uint16_t* codebook;
   const uint16_t* Xp;   // activations in permuted order, [M][d_in]
   uint16_t* Y;
+  float* partial;       // split-K partial sums [S][M][rt * 64] (S > 1)
   int64_t ldy;
   int32_t d_out, d_in, M, L;
   int32_t rt, ng;
+  int32_t S, gs;        // column splits (blockIdx.z) and groups per split
 };
 
 __host__ __device__ inline uint32_t prefill_slab_offset(int L) {
@@ -406,16 +408,21 @@ __device__ void prefill_body(const PrefillArgs& A, uint8_t* smem) {
   const bool tile_ok = rt < A.rt;
   const int m0 = blockIdx.y * kPfRows;
   const int mrows = min(A.M - m0, kPfRows);
-  const int ng = A.ng;
+  const int g0 = blockIdx.z * A.gs;          // first column group of this split
+  const int ng = min(A.ng - g0, A.gs);       // groups of this split
   uint8_t* cb = smem;
   uint2* smask = reinterpret_cast<uint2*>(smem + kK * 256);
   _Float16* slab0 = reinterpret_cast<_Float16*>(smem + prefill_slab_offset(L));
 
   const __amdgpu_buffer_rsrc_t cb_rs = view(A.codebook, kK * 16u);
+  // the views start at the split's first group; words and activations of groups past the
+  // split's last are never addressed (offsets point outside both views)
   const __amdgpu_buffer_rsrc_t w_rs =
-      view(A.packed + (int64_t)rt * ng * kBlockBytes, tile_ok ? (uint32_t)(ng * kBlockBytes) : 0u);
+      view(A.packed + ((int64_t)rt * A.ng + g0) * kBlockBytes,
+           tile_ok ? (uint32_t)(ng * kBlockBytes) : 0u);
   const __amdgpu_buffer_rsrc_t x_rs =
-      view(A.Xp + (int64_t)m0 * A.d_in, (uint32_t)(mrows * A.d_in * 2));
+      view(A.Xp + (int64_t)m0 * A.d_in + g0 * kGroupCols,
+           (uint32_t)((mrows * A.d_in - g0 * kGroupCols) * 2));
   // per-lane byte offsets, fixed for the whole loop; the group adds a uniform amount
   const uint32_t wa0 = kPlaneA + r0 * 16, wb0 = kPlaneB + r0 * 16, ws0 = kSidePlane + r0 * 8;
   // chunk i of a thread: activation row (tid / 16) + 16 i, channels 8 (tid % 16) .. +7
@@ -511,6 +518,29 @@ __device__ void prefill_body(const PrefillArgs& A, uint8_t* smem) {
   // D layout: lane holds weight row l % 32 of each subtile and activation rows
   // 8 (v / 4) + 4 (l / 32) + v % 4 of each 32-row block.
   if (!tile_ok) return;
+  if (A.S > 1) {
+    // one split's fp32 sums, stored as the accumulators lie: wave tile (split, block, rt) owns
+    // 2 kQ 16 x 64 floats, element (t, q, v) of lane l at ((t kQ + q) 16 + v) 64 + l; a second
+    // kernel adds the splits in order
+    constexpr int kTileFloats = 2 * kQ * 16 * 64;
+    float* base = A.partial +
+                  (((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * A.rt + rt) * kTileFloats;
+    const __amdgpu_buffer_rsrc_t p_rs = view(base, kTileFloats * 4u);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int q = 0; q < kQ; ++q)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          // copy the element out first: a bit cast taken straight from a vector element reads
+          // the vector's first element (clang, ext_vector_type)
+          const float f = acc[t][q][v];
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, f), p_rs,
+                                                (uint32_t)lane * 4u,
+                                                ((t * kQ + q) * 16 + v) * 256, 0);
+        }
+    return;
+  }
   const __amdgpu_buffer_rsrc_t y_rs =
       view(A.Y + (int64_t)m0 * A.ldy, (uint32_t)((int64_t)mrows * A.ldy * 2));
 #pragma unroll
@@ -529,35 +559,119 @@ __device__ void prefill_body(const PrefillArgs& A, uint8_t* smem) {
   }
 }
 
-template <int kQ>
-__global__ void __launch_bounds__(kPfThreads) prefill_kernel(PrefillArgs A) {
+// One kernel per codebook size: with a switch over L inside one kernel the compiler hoists the
+// first activation loads above the switch and spills them. The 128-row variant fits in 256
+// registers, which lets two waves share a SIMD (two workgroups per compute unit when the LDS
+// allows).
+template <int L, int kQ>
+__global__ void __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(kQ == 4 ? 2 : 1, 2)))
+prefill_kernel(PrefillArgs A) {
   extern __shared__ __align__(16) uint8_t smem[];
-  switch (A.L) {
-    case 4: prefill_body<4, kQ>(A, smem); break;
-    case 5: prefill_body<5, kQ>(A, smem); break;
-    case 6: prefill_body<6, kQ>(A, smem); break;
-    case 7: prefill_body<7, kQ>(A, smem); break;
-    default: prefill_body<8, kQ>(A, smem); break;
+  prefill_body<L, kQ>(A, smem);
+}
+
+typedef void (*PrefillFn)(PrefillArgs);
+
+// kq = 8 exists for L <= 6 only: larger codebooks leave no room for two 256-row slabs
+PrefillFn prefill_fn(int L, int kq) {
+  if (kq == 8) {
+    switch (L) {
+      case 4: return prefill_kernel<4, 8>;
+      case 5: return prefill_kernel<5, 8>;
+      default: return prefill_kernel<6, 8>;
+    }
+  }
+  switch (L) {
+    case 4: return prefill_kernel<4, 4>;
+    case 5: return prefill_kernel<5, 4>;
+    case 6: return prefill_kernel<6, 4>;
+    case 7: return prefill_kernel<7, 4>;
+    default: return prefill_kernel<8, 4>;
   }
 }
 
-// Activation blocks per workgroup: 8 (each decoded subvector feeds 8 MFMAs) when two 256-row slabs
-// fit next to the codebook and the grid of 256-row workgroups still covers half the compute
-// units; else 4 (measured: 9728x2560 at M = 1024 runs 105 us with 8, 123 us with 4; at M = 512
-// the 8-block grid is too small and takes 98 us against 70 us).
-int prefill_blocks(int L, int rt, int M) {
-  const size_t lds8 = prefill_slab_offset(L) + 2 * (size_t)PfShape<8>::kSlab;
-  const int64_t wgs8 = (int64_t)ceil_div(rt, kPfWaves) * ceil_div(M, PfShape<8>::kRows);
-  return (lds8 <= 160 * 1024 && 2 * wgs8 >= device_cu_count()) ? 8 : 4;
+// Split sums of the prefill kernel, one output per thread: thread i reads element i of every
+// split's plane (laid out as the kernel's accumulators, 64 x rows floats per wave tile and block)
+// and writes Y[m][n] = fp16(partial[0] + ... + partial[S-1]), added in split order.
+__global__ void __launch_bounds__(256) prefill_reduce_kernel(const float* __restrict__ partial,
+                                                             int S, int64_t plane, int rows,
+                                                             int rt, int M, int d_out,
+                                                             uint16_t* __restrict__ Y, int64_t ldy) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= plane) return;
+  const int tile = 64 * rows;                 // floats of one wave tile and activation block
+  const int64_t c = i / tile;
+  const int e = (int)(i - c * tile);
+  const int lane = e & 63;
+  const int v = (e >> 6) & 15;
+  const int tq = e >> 10;                     // t kQ + q
+  const int kq = rows / 32;
+  const int t = tq / kq, q = tq - t * kq;
+  const int r = (int)(c % rt);
+  const int b = (int)(c / rt);
+  const int n = r * kTileRows + t * 32 + (lane & 31);
+  const int m = b * rows + q * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+  if (m >= M || n >= d_out) return;
+  float sum = partial[i];
+  for (int sp = 1; sp < S; ++sp) sum += partial[sp * plane + i];
+  Y[(int64_t)m * ldy + n] = f2h(sum);
 }
 
-// The prefill kernel keeps one wave per SIMD busy for a whole column loop, so it pays off only
-// when its grid covers at least half the compute units; otherwise the small-batch kernel's
-// split-K spreads the same work wider (measured on 9728x2560 and 2560x9728, M = 128 ... 1024).
-bool use_prefill(int d_out, int M) {
-  if (M < kPrefillMinRows) return false;
-  const int64_t wgs = (int64_t)ceil_div(ceil_div(d_out, kTileRows), kPfWaves) * ceil_div(M, 128);
-  return 2 * wgs >= device_cu_count();
+// Launch shape of the prefill kernel: kq 32-row activation blocks per workgroup, S column splits
+// of gs groups. kq = 0 means the small-batch kernel runs instead.
+struct PfPlan {
+  int kq = 0;
+  int S = 1;
+  int gs = 0;
+};
+
+size_t prefill_lds(int L, int kq) {
+  return prefill_slab_offset(L) +
+         2 * (size_t)(kq == 8 ? PfShape<8>::kSlab : PfShape<4>::kSlab);
+}
+
+// From kPrefillMinRows rows on (measured on 9728x2560 and 2560x9728, M = 128 ... 1024, every
+// kq and split count):
+//  - kq = 8 (each decoded subvector feeds 8 MFMAs, one workgroup per compute unit) when more than
+//    128 rows come, two 256-row slabs fit beside the codebook and its grid covers at least half
+//    the compute units; it never gained from splits.
+//  - else kq = 4, with the column groups split until the grid reaches one workgroup per compute
+//    unit (at least two groups per split). Wider grids lost: the splits' fp32 sums cost 8 bytes
+//    per output and split.
+//  - Below 256 rows the small-batch kernel wins unless the split is deep (grid of 128-row blocks
+//    at most an eighth of the compute units).
+PfPlan prefill_plan(int L, int d_out, int d_in, int M) {
+  PfPlan P;
+  if (M < kPrefillMinRows) return P;
+  const int64_t cus = device_cu_count();
+  const int ng = d_in / kGroupCols;
+  const int64_t wx = ceil_div(ceil_div(d_out, kTileRows), kPfWaves);
+  const int64_t wgs8 = wx * ceil_div(M, PfShape<8>::kRows);
+  if (M > PfShape<4>::kRows && prefill_lds(L, 8) <= 160 * 1024 && 2 * wgs8 >= cus) {
+    P.kq = 8;
+    P.gs = ng;
+    return P;
+  }
+  const int64_t wgs = wx * ceil_div(M, PfShape<4>::kRows);
+  if (M < 256 && 8 * wgs > cus) return P;
+  P.kq = 4;
+  int64_t S = cus / wgs;
+  if (S > ng / 2) S = ng / 2;
+  if (S < 1) S = 1;
+  P.gs = ceil_div(ng, (int)S);
+  P.S = ceil_div(ng, P.gs);
+  return P;
+}
+
+// floats of one split's partial sums: every wave tile of every activation block
+int64_t prefill_plane(const PfPlan& P, int d_out, int M) {
+  const int rows = 32 * P.kq;
+  return (int64_t)ceil_div(M, rows) * rows * ceil_div(d_out, kTileRows) * kTileRows;
+}
+
+size_t prefill_partial_bytes(const PfPlan& P, int d_out, int M) {
+  if (P.S <= 1) return 0;
+  return ((size_t)P.S * prefill_plane(P, d_out, M) * 4 + 255) / 256 * 256;
 }
 
 int tiles_for(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
@@ -596,7 +710,9 @@ size_t permuted_bytes(int M, int d_in) {
 
 size_t workspace_for(const GemmArgs& A) {
   const size_t xp = permuted_bytes(A.M, A.d_in);
-  if (use_prefill(A.d_out, A.M) || A.S == 1) return xp;
+  const PfPlan pf = prefill_plan(A.L, A.d_out, A.d_in, A.M);
+  if (pf.kq) return xp + prefill_partial_bytes(pf, A.d_out, A.M);
+  if (A.S == 1) return xp;
   const size_t part = (size_t)A.mchunks * A.S * A.mrows_chunk * A.rt * kTileRows * 4;
   const size_t cnt = (size_t)A.mchunks * A.rpairs * 4;
   return xp + (part + cnt + 255) / 256 * 256;
@@ -653,7 +769,8 @@ int sage_gemm_small(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, u
     if (!aligned(ws, 256)) return SAGE_ERR_ALIGN;
   }
   char* wsb = static_cast<char*>(ws);
-  if (A.S > 1) {
+  const PfPlan pf = prefill_plan(A.L, A.d_out, A.d_in, M);
+  if (A.S > 1 && !pf.kq) {
     A.partial = reinterpret_cast<float*>(wsb + xp_bytes);
     A.counters = reinterpret_cast<uint32_t*>(
         wsb + xp_bytes + (size_t)A.mchunks * A.S * A.mrows_chunk * A.rt * kTileRows * 4);
@@ -665,7 +782,7 @@ int sage_gemm_small(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, u
     const int64_t n = (int64_t)M * A.d_in;
     hipLaunchKernelGGL(permute_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, hs,
                        X, (int64_t)ldx, m->pi, A.d_in, M, Xp);
-    if (use_prefill(A.d_out, M)) {
+    if (pf.kq) {
       PrefillArgs P{};
       P.packed = A.packed;
       P.codebook = A.codebook;
@@ -678,22 +795,24 @@ int sage_gemm_small(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, u
       P.L = A.L;
       P.rt = A.rt;
       P.ng = A.ng;
-      static bool pf_attr = false;
-      if (!pf_attr) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<4>),
+      P.S = pf.S;
+      P.gs = pf.gs;
+      if (pf.S > 1) P.partial = reinterpret_cast<float*>(wsb + xp_bytes);
+      const PrefillFn fn = prefill_fn(A.L, pf.kq);
+      static bool attr_set[2][9] = {};
+      if (!attr_set[pf.kq == 8][A.L]) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<8>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        pf_attr = true;
+        attr_set[pf.kq == 8][A.L] = true;
       }
-      if (prefill_blocks(A.L, A.rt, M) == 8) {
-        const dim3 grid((unsigned)ceil_div(A.rt, kPfWaves), (unsigned)ceil_div(M, PfShape<8>::kRows));
-        const size_t lds = prefill_slab_offset(A.L) + 2 * (size_t)PfShape<8>::kSlab;
-        hipLaunchKernelGGL(prefill_kernel<8>, grid, dim3(kPfThreads), lds, hs, P);
-      } else {
-        const dim3 grid((unsigned)ceil_div(A.rt, kPfWaves), (unsigned)ceil_div(M, PfShape<4>::kRows));
-        const size_t lds = prefill_slab_offset(A.L) + 2 * (size_t)PfShape<4>::kSlab;
-        hipLaunchKernelGGL(prefill_kernel<4>, grid, dim3(kPfThreads), lds, hs, P);
+      const dim3 grid((unsigned)ceil_div(A.rt, kPfWaves), (unsigned)ceil_div(M, 32 * pf.kq),
+                      (unsigned)pf.S);
+      hipLaunchKernelGGL(fn, grid, dim3(kPfThreads), prefill_lds(A.L, pf.kq), hs, P);
+      if (pf.S > 1) {
+        const int64_t plane = prefill_plane(pf, A.d_out, M);
+        hipLaunchKernelGGL(prefill_reduce_kernel, dim3((unsigned)((plane + 255) / 256)), dim3(256),
+                           0, hs, P.partial, pf.S, plane, 32 * pf.kq, A.rt, M, A.d_out, Y,
+                           (int64_t)ldy);
       }
       return hip_status();
     }

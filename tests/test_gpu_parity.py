@@ -458,6 +458,29 @@ def test_gemm_prefill_kernel(d_out, d_in, M, K, V):
     assert np.all(err <= tol)
 
 
+@pytest.mark.parametrize("d_out,d_in,M,K,V,ldy", [(130, 1408, 130, 32, 5, 130), (130, 1280, 300, 256, 2, 136),
+                                                   (640, 9728, 128, 16, 6, 640), (200, 2432, 257, 64, 4, 203)])
+def test_gemm_prefill_split(d_out, d_in, M, K, V, ldy):
+    """Grids too narrow for the compute units: the prefill kernel splits the column groups
+    (ragged last split, 128- and 256-row activation blocks, output rows wider than d_out) and a
+    second kernel adds the splits; a repeated call gives the same bits."""
+    import torch
+    rng = W.rng_for(146, d_out, d_in, M)
+    c = W.draw_codes(rng, d_out, d_in, K, V)
+    X = W.draw_x(rng, (M, d_in))
+    p = upload_pack(c)
+    Xd = torch.from_numpy(X).cuda()
+    Ybig = torch.full((M, ldy), 7.0, dtype=torch.float16, device="cuda")
+    sage.gemm_small(p, Xd, Y=Ybig[:, :d_out])
+    Y2 = sage.gemm_small(p, Xd)
+    torch.cuda.synchronize()
+    Yb = _np(Ybig)
+    assert np.all(Yb[:, d_out:] == np.float16(7.0))
+    Y = Yb[:, :d_out]
+    assert np.array_equal(Y.view(np.uint16), _np(Y2).view(np.uint16))
+    check_gemm(f"split {d_out}x{d_in} K={K} M={M}", c, X, torch.from_numpy(np.ascontiguousarray(Y)))
+
+
 def test_gemm_strided_rows():
     import torch
     c = W.draw_codes(W.rng_for(141), 200, 512, 32, 5)
