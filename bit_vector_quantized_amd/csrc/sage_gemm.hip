@@ -15,6 +15,8 @@
 // activations of its columns are staged once in LDS (gathered through pi, §3.2) and shared by both
 // tiles, the two column parts add their accumulators in LDS. All packed-weight loads of a wave are
 // issued up front through range-checked buffer loads, as in the batch-one kernel.
+#include <algorithm>
+
 #include "sage_internal.hpp"
 
 namespace sage {
@@ -62,18 +64,126 @@ __device__ inline uint2 nibble_masks(uint32_t n) {
 }
 
 // X[:, pi] for M rows into a dense [M][d_in] buffer (the reorder the paper does once per
-// projection before prefill, §3.5).
+// projection before prefill, §3.5). A workgroup copies kR whole rows of X into LDS (all its
+// 16-byte loads issued before any is stored), then each thread gathers 8 consecutive outputs of
+// the workgroup's column range (blockIdx.y, `units` 8-column units each) through pi from LDS, pi
+// read once for all kR rows, and writes them as one 16-byte store. kR * J <= 16, J = row loads
+// per thread = ceil(d_in / 2048).
+constexpr int kPermLoads = 16;
+constexpr int kPermLdsMinRows = 128;
+
+template <int kR>
 __global__ void __launch_bounds__(256) permute_rows_kernel(const uint16_t* __restrict__ X,
                                                            int64_t ldx,
                                                            const int32_t* __restrict__ pi,
-                                                           int d_in, int M,
+                                                           int d_in, int M, int units,
                                                            uint16_t* __restrict__ Xp) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= (int64_t)M * d_in) return;
-  const int m = (int)(t / d_in);
-  const int p = (int)(t - (int64_t)m * d_in);
+  constexpr int kJ = kPermLoads / kR;
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
+  const int tid = threadIdx.x;
+  const int m0 = blockIdx.x * kR;
+  const int nr = min(M - m0, kR);
+  const int row_units = d_in >> 3;
+  const uint32_t last = (uint32_t)d_in - 1u;
+  const int c0 = blockIdx.y * units + tid;
+  const int c1 = min(row_units, (int)(blockIdx.y + 1) * units);
+  // Every load is issued unconditionally through a range-checked view (an offset outside the view
+  // reads zeros without touching memory), so all of them are in flight together: the permutation
+  // entries of the thread's first two 8-column units and its 16-byte chunks of the kR rows.
+  const __amdgpu_buffer_rsrc_t pi_rs = view(pi, pi ? (uint32_t)d_in * 4u : 0u);
+  u32x4 pv[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = c0 + i * 256;
+    const uint32_t off = c < c1 ? (uint32_t)c * 32u : kNowhere;
+    pv[i][0] = __builtin_amdgcn_raw_buffer_load_b128(pi_rs, off, 0, 0);
+    pv[i][1] = __builtin_amdgcn_raw_buffer_load_b128(pi_rs, off + 16u, 0, 0);
+  }
+  const __amdgpu_buffer_rsrc_t x_rs =
+      view(X + (int64_t)m0 * ldx, (uint32_t)(((int64_t)(nr - 1) * ldx + d_in) * 2));
+  u32x4 v[kR][kJ];
+#pragma unroll
+  for (int r = 0; r < kR; ++r)
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const int cc = tid + j * 256;
+      const uint32_t off =
+          (r < nr && cc < row_units) ? (uint32_t)(((int64_t)r * ldx + cc * 8) * 2) : kNowhere;
+      v[r][j] = __builtin_amdgcn_raw_buffer_load_b128(x_rs, off, 0, 0);
+    }
+#pragma unroll
+  for (int r = 0; r < kR; ++r)
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const int cc = tid + j * 256;
+      if (r < nr && cc < row_units) *reinterpret_cast<u32x4*>(xs + r * d_in + cc * 8) = v[r][j];
+    }
+  int idx[2][8];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = c0 + i * 256;
+      idx[i][j] = pi ? (int)min(pv[i][j >> 2][j & 3], last) : c * 8 + j;
+    }
+  __syncthreads();
+  for (int c = c0, i = 0; c < c1; c += 256, ++i) {
+    int id[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      id[j] = i < 2 ? idx[i & 1][j] : (pi ? (int)min((uint32_t)pi[c * 8 + j], last) : c * 8 + j);
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      if (r >= nr) break;
+      const uint16_t* xr = xs + r * d_in;
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = (uint32_t)xr[id[2 * j]] | ((uint32_t)xr[id[2 * j + 1]] << 16);
+      *reinterpret_cast<uint4*>(Xp + (int64_t)(m0 + r) * d_in + c * 8) =
+          make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+// Permute launch: rows per workgroup kR (a power of two with kR * J <= 16, at most M / CUs) and
+// column ranges, so the grid reaches about two workgroups per compute unit while each workgroup
+// still writes at least 256 columns (every workgroup stages its whole rows: few rows spread over
+// more workgroups measured faster than one workgroup per row), and no thread gathers more than
+// two 8-column units. kR = 0 (X not 16-byte aligned, or rows wider than 32768)
+// selects the element-wise gather below, and so do fewer than kPermLdsMinRows rows (measured on
+// 2560 and 9728 columns: at 16 and 64 rows the GEMM ran up to 1 us faster after the element-wise
+// gather, at 1024 rows the staged reorder took 9 us instead of 37 us on 9728 columns).
+struct PermPlan {
+  int rows = 0, ranges = 1, units = 0;
+};
+
+PermPlan permute_plan(int d_in, int M, bool aligned16) {
+  PermPlan P;
+  const int J = ceil_div(d_in, 2048);
+  if (!aligned16 || J > kPermLoads || M < kPermLdsMinRows) return P;
+  const int cus = device_cu_count();
+  const int want = std::max(1, std::min(kPermLoads / J, M / cus));
+  P.rows = want >= 8 ? 8 : (want >= 4 ? 4 : (want >= 2 ? 2 : 1));
+  const int wg_rows = ceil_div(M, P.rows);
+  P.ranges = std::max(1, std::min(ceil_div(2 * cus, wg_rows), d_in / 256));
+  P.ranges = std::max(P.ranges, ceil_div(d_in / 8, 512));  // at most two units per thread
+  P.units = ceil_div(d_in / 8, P.ranges);
+  P.ranges = ceil_div(d_in / 8, P.units);
+  return P;
+}
+
+__global__ void __launch_bounds__(256) permute_gather_kernel(const uint16_t* __restrict__ X,
+                                                             int64_t ldx,
+                                                             const int32_t* __restrict__ pi,
+                                                             int d_in, int M,
+                                                             uint16_t* __restrict__ Xp) {
+  const int m = blockIdx.x;
+  const int p = blockIdx.y * 256 + threadIdx.x;
+  if (p >= d_in) return;
   const int src = pi ? (int)min((uint32_t)pi[p], (uint32_t)d_in - 1u) : p;
-  Xp[t] = X[(int64_t)m * ldx + src];
+  Xp[(int64_t)m * d_in + p] = X[(int64_t)m * ldx + src];
 }
 
 __device__ inline uint32_t mul_pair(uint32_t c, half2_t r) {
@@ -329,22 +439,22 @@ __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs A) {
 
 // ------------------------------------------------------------------------------------------------
 // Prefill-sized batches (SAGE paper §3.5 / Fig. 6b: decode each weight once per output tile and
-// reuse it across many activation rows). A wavefront owns one 64-row weight tile and 128
-// activation rows, as 2 x 4 tiles of v_mfma_f32_32x32x16_f16 (128 fp32 accumulators per lane).
-// In the B operand lane l supplies weight row l % 32 of a 32-row subtile and channels
-// 8 (l / 32) .. +7 of the 16-channel step, i.e. one subvector: step s of a group uses subvectors
-// 2s (lanes 0-31) and 2s + 1 (lanes 32-63). A workgroup (4 waves, 4 weight tiles) shares a
-// double-buffered activation slab [128 rows][128 channels] in LDS; the loop over column groups
-// prefetches the next group's packed words and activations into registers while the current
-// group runs, so every weight is decoded once per 128 activation rows.
+// reuse it across many activation rows). A wavefront owns one 64-row weight tile and kQ 32-row
+// blocks of activations, as 2 x kQ tiles of v_mfma_f32_32x32x16_f16 (16 fp32 accumulators per
+// lane and tile). In the B operand lane l supplies weight row l % 32 of a 32-row subtile and
+// channels 8 (l / 32) .. +7 of the 16-channel step, i.e. one subvector: step s of a group uses
+// subvectors 2s (lanes 0-31) and 2s + 1 (lanes 32-63). A workgroup (4 waves, 4 weight tiles)
+// shares a double-buffered activation slab [32 kQ rows][128 channels] in LDS, filled by
+// buffer-to-LDS loads one group ahead, so every weight is decoded once per 32 kQ activation rows.
 constexpr int kPfWaves = 4;
 constexpr int kPfThreads = kPfWaves * 64;
-constexpr int kPfStride = kGroupCols + 8;             // fp16 per staged activation row (padded)
-// kQ 32-row blocks of activations per workgroup (4 or 8): rows, slab bytes, 16-byte chunks/thread
+// kQ 32-row blocks of activations per workgroup (4 or 8): rows and slab bytes. Slab rows are
+// 256 bytes unpadded; 16-byte chunk c of row R sits at chunk slot c ^ (R % 16), so the 16 rows a
+// quarter-wave reads in one operand load hit 16 different slots (all 64 banks).
 template <int kQ> struct PfShape {
   static constexpr int kRows = 32 * kQ;
-  static constexpr int kSlab = kRows * kPfStride * 2;
-  static constexpr int kChunks = kRows * kGroupCols / 8 / kPfThreads;
+  static constexpr int kSlab = kRows * kGroupCols * 2;
+  static constexpr int kLoads = kRows * kGroupCols * 2 / 1024 / kPfWaves;  // 1 KiB loads per wave
 };
 
 typedef float float16_t __attribute__((ext_vector_type(16)));
@@ -354,7 +464,7 @@ struct PrefillArgs {
   const uint16_t* codebook;
   const uint16_t* Xp;   // activations in permuted order, [M][d_in]
   uint16_t* Y;
-  float* partial;       // split-K partial sums [S][M][rt * 64] (S > 1)
+  float* partial;       // split-K partial sums, see the split store below (S > 1)
   int64_t ldy;
   int32_t d_out, d_in, M, L;
   int32_t rt, ng;
@@ -371,26 +481,38 @@ struct RowWords {
   u32x2 side;
 };
 
+// First half of a subvector decode: the codeword replica, the two sign masks and the radius.
+// The LDS reads are only issued here; decode_finish consumes them a pipeline step later.
+struct Fetched {
+  uint4 c;
+  uint2 mlo, mhi;
+  half2_t r2;
+};
+
 template <int L>
-__device__ __forceinline__ half8_t decode_b(uint32_t P, uint32_t X, uint32_t G, int s, int h,
-                                            const uint8_t* cb, const uint2* smask,
-                                            uint32_t laneoff) {
+__device__ __forceinline__ Fetched decode_fetch(const RowWords& w, int s, int h, const uint8_t* cb,
+                                                const uint2* smask, uint32_t laneoff) {
   constexpr uint32_t kK = 1u << L;
+  const uint32_t P = s < 4 ? w.a[s & 3] : w.b[s & 3];
+  const uint32_t X = w.side[0], G = w.side[1];
   // subvector 2s + h of the group: pair s, half a (h = 0) or b (h = 1)
   const uint32_t f = (P >> (h ? 18 : 8)) & 1023u;
   const uint32_t lo = h ? (P & 15u) : ((P >> 4) & 15u);
   const uint32_t hi = h ? ((X >> (4 * s)) & 15u) : (P >> 28);
-  const float mu = h2f(G);
-  const float dl = h2f(G >> 16);
-  const float r = fmaf((float)(f >> L), dl, mu);
+  const float r = fmaf((float)(f >> L), h2f(G >> 16), h2f(G));
   const _Float16 rh = (_Float16)r;
-  const half2_t r2 = half2_t{rh, rh};
-  const uint4 c = *reinterpret_cast<const uint4*>(cb + (f & (kK - 1u)) * 256 + laneoff);
-  const uint2 mlo = smask[lo];
-  const uint2 mhi = smask[hi];
+  Fetched o;
+  o.r2 = half2_t{rh, rh};
+  o.c = *reinterpret_cast<const uint4*>(cb + (f & (kK - 1u)) * 256 + laneoff);
+  o.mlo = smask[lo];
+  o.mhi = smask[hi];
+  return o;
+}
+
+__device__ __forceinline__ half8_t decode_finish(const Fetched& d) {
   return __builtin_bit_cast(
-      half8_t, make_uint4(mul_pair(c.x ^ mlo.x, r2), mul_pair(c.y ^ mlo.y, r2),
-                          mul_pair(c.z ^ mhi.x, r2), mul_pair(c.w ^ mhi.y, r2)));
+      half8_t, make_uint4(mul_pair(d.c.x ^ d.mlo.x, d.r2), mul_pair(d.c.y ^ d.mlo.y, d.r2),
+                          mul_pair(d.c.z ^ d.mhi.x, d.r2), mul_pair(d.c.w ^ d.mhi.y, d.r2)));
 }
 
 template <int L, int kQ>
@@ -398,7 +520,7 @@ __device__ void prefill_body(const PrefillArgs& A, uint8_t* smem) {
   constexpr uint32_t kK = 1u << L;
   constexpr int kPfRows = PfShape<kQ>::kRows;
   constexpr int kPfSlab = PfShape<kQ>::kSlab;
-  constexpr int kPfChunks = PfShape<kQ>::kChunks;
+  constexpr int kPfLoads = PfShape<kQ>::kLoads;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -412,7 +534,7 @@ __device__ void prefill_body(const PrefillArgs& A, uint8_t* smem) {
   const int ng = min(A.ng - g0, A.gs);       // groups of this split
   uint8_t* cb = smem;
   uint2* smask = reinterpret_cast<uint2*>(smem + kK * 256);
-  _Float16* slab0 = reinterpret_cast<_Float16*>(smem + prefill_slab_offset(L));
+  uint8_t* slab0 = smem + prefill_slab_offset(L);
 
   const __amdgpu_buffer_rsrc_t cb_rs = view(A.codebook, kK * 16u);
   // the views start at the split's first group; words and activations of groups past the
@@ -425,19 +547,23 @@ __device__ void prefill_body(const PrefillArgs& A, uint8_t* smem) {
            (uint32_t)((mrows * A.d_in - g0 * kGroupCols) * 2));
   // per-lane byte offsets, fixed for the whole loop; the group adds a uniform amount
   const uint32_t wa0 = kPlaneA + r0 * 16, wb0 = kPlaneB + r0 * 16, ws0 = kSidePlane + r0 * 8;
-  // chunk i of a thread: activation row (tid / 16) + 16 i, channels 8 (tid % 16) .. +7
-  const uint32_t xbase = (uint32_t)(((tid >> 4) * A.d_in + (tid & 15) * 8) * 2);
-  const uint32_t xstep = (uint32_t)(16 * A.d_in * 2);
-  const uint32_t sbase = (uint32_t)(((tid >> 4) * kPfStride + (tid & 15) * 8) * 2);
-  constexpr uint32_t kSStep = 16 * kPfStride * 2;
+  // Buffer-to-LDS loads: lane l of a 1 KiB load j writes slot l % 16 of slab row 4 j + l / 16,
+  // so it fetches chunk (l % 16) ^ ((4 j + l / 16) % 16) of that row; the chunk depends on j % 4.
+  const uint32_t row_bytes = (uint32_t)A.d_in * 2u;
+  uint32_t xl[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    xl[t] = (uint32_t)(lane >> 4) * row_bytes +
+            (((uint32_t)(lane & 15) ^ ((4u * t + (uint32_t)(lane >> 4)) & 15u)) << 4);
+  // operand loads: row q 32 + r0, chunk 2 s + h at slot (2 s) ^ (h ^ r0 % 16)
+  const uint32_t a_row = (uint32_t)r0 * 256u;
+  const uint32_t a_hm = ((uint32_t)h ^ (uint32_t)(r0 & 15)) << 4;
 
   const u32x4 cw = __builtin_amdgcn_raw_buffer_load_b128(cb_rs, tid * 16, 0, 0);
   // Packed words run two groups ahead through a three-deep register ring (group g computes from
   // slot g % 3; no slot is copied, so no wait covers a later group). Activations run one group
-  // ahead (they come from L2): loaded at the start of a group, staged in LDS at its end, and
-  // issued before the packed words so that waiting for them does not wait for the words.
+  // ahead, loaded straight into the other slab buffer.
   RowWords wr[3][2];
-  u32x4 xr[kPfChunks];
 #define SAGE_PF_WORDS(slot, grp)                                                              \
   {                                                                                          \
     const uint32_t wg_ = (grp) < ng ? (uint32_t)(grp) * kBlockBytes : kNowhere;              \
@@ -450,13 +576,14 @@ __device__ void prefill_body(const PrefillArgs& A, uint8_t* smem) {
 #define SAGE_PF_X(grp)                                                                       \
   {                                                                                          \
     const uint32_t xg_ = (grp) < ng ? (uint32_t)(grp) * (kGroupCols * 2) : kNowhere;         \
-    _Pragma("unroll") for (int i = 0; i < kPfChunks; ++i)                                    \
-      xr[i] = __builtin_amdgcn_raw_buffer_load_b128(x_rs, xg_ + xbase + i * xstep, 0, 0);    \
+    uint8_t* dst_ = slab0 + ((grp) & 1) * kPfSlab + wave * (kPfLoads * 1024);                \
+    _Pragma("unroll") for (int i = 0; i < kPfLoads; ++i) {                                   \
+      const uint32_t row_ = (uint32_t)(4 * (wave * kPfLoads + i));                           \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(                                              \
+          x_rs, (__attribute__((address_space(3))) void*)(dst_ + i * 1024), 16,              \
+          xg_ + row_ * row_bytes + xl[i & 3], 0, 0, 0);                                      \
+    }                                                                                        \
   }
-#define SAGE_PF_STAGE(buf)                                                                   \
-  _Pragma("unroll") for (int i = 0; i < kPfChunks; ++i)                                      \
-    *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(slab0) + (buf) * kPfSlab + sbase +  \
-                              i * kSStep) = xr[i];
   SAGE_PF_X(0)
   SAGE_PF_WORDS(0, 0)
   SAGE_PF_WORDS(1, 1)
@@ -465,7 +592,8 @@ __device__ void prefill_body(const PrefillArgs& A, uint8_t* smem) {
     for (int r = 0; r < 16; ++r) *reinterpret_cast<u32x4*>(cb + tid * 256 + r * 16) = cw;
   }
   if (tid < 16) smask[tid] = nibble_masks((uint32_t)tid);
-  SAGE_PF_STAGE(0)
+  // the first slab has landed once only the two word groups are outstanding
+  asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
   __syncthreads();
 
   float16_t acc[2][kQ];
@@ -477,30 +605,49 @@ __device__ void prefill_body(const PrefillArgs& A, uint8_t* smem) {
       for (int v = 0; v < 16; ++v) acc[t][q][v] = 0.0f;
   const uint32_t laneoff = (uint32_t)(lane & 15) * 16u;
 
-  // one group: activations of g + 1 and words of g + 2 (slot (k + 2) % 3) in flight, multiply
-  // group g (slot k, LDS buffer g & 1), stage g + 1 into the other buffer
+  // One group, software-pipelined over its 8 steps: while the MFMAs of step s run, the operand
+  // loads of step s + 1 and the codebook/mask loads of step s + 2 are in flight and step s + 1's
+  // decode finishes on the vector ALU. Activations of g + 1 go to the other slab buffer and the
+  // words of g + 2 into ring slot (k + 2) % 3 at the start; at the end every wave waits for its
+  // slab loads (all but the 6 word loads just issued) and meets the others at the barrier.
 #define SAGE_PF_GROUP(k)                                                                      \
   {                                                                                           \
     const int gg = g + (k);                                                                   \
     SAGE_PF_X(gg + 1)                                                                         \
     SAGE_PF_WORDS(((k) + 2) % 3, gg + 2)                                                      \
-    const uint8_t* slab = reinterpret_cast<const uint8_t*>(slab0) + (gg & 1) * kPfSlab;       \
+    const uint8_t* abuf = slab0 + (gg & 1) * kPfSlab + a_row;                                 \
+    Fetched fd[2][2];                                                                         \
+    half8_t bv[2][2];                                                                         \
+    half8_t av[2][kQ];                                                                        \
+    _Pragma("unroll") for (int t = 0; t < 2; ++t) {                                           \
+      fd[0][t] = decode_fetch<L>(wr[k][t], 0, h, cb, smask, laneoff);                         \
+      fd[1][t] = decode_fetch<L>(wr[k][t], 1, h, cb, smask, laneoff);                         \
+    }                                                                                         \
+    _Pragma("unroll") for (int q = 0; q < kQ; ++q)                                            \
+      av[0][q] = *reinterpret_cast<const half8_t*>(abuf + q * 8192 + (a_hm ^ 0u));            \
+    _Pragma("unroll") for (int t = 0; t < 2; ++t) bv[0][t] = decode_finish(fd[0][t]);         \
+    __builtin_amdgcn_sched_barrier(0);                                                        \
     _Pragma("unroll") for (int s = 0; s < 8; ++s) {                                           \
-      half8_t b[2];                                                                           \
-      _Pragma("unroll") for (int t = 0; t < 2; ++t) {                                         \
-        const uint32_t P = s < 4 ? wr[k][t].a[s] : wr[k][t].b[s - 4];                         \
-        b[t] = decode_b<L>(P, wr[k][t].side[0], wr[k][t].side[1], s, h, cb, smask, laneoff);  \
+      if (s + 1 < 8) {                                                                        \
+        _Pragma("unroll") for (int q = 0; q < kQ; ++q)                                        \
+          av[(s + 1) & 1][q] = *reinterpret_cast<const half8_t*>(                             \
+              abuf + q * 8192 + (a_hm ^ (uint32_t)(32 * (s + 1))));                           \
       }                                                                                       \
-      _Pragma("unroll") for (int q = 0; q < kQ; ++q) {                                        \
-        const half8_t a = *reinterpret_cast<const half8_t*>(                                  \
-            slab + ((q * 32 + r0) * kPfStride + s * 16 + 8 * h) * 2);                         \
+      if (s + 2 < 8) {                                                                        \
         _Pragma("unroll") for (int t = 0; t < 2; ++t)                                         \
-          acc[t][q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b[t], acc[t][q], 0, 0, 0);    \
+          fd[s & 1][t] = decode_fetch<L>(wr[k][t], s + 2, h, cb, smask, laneoff);             \
+      }                                                                                       \
+      _Pragma("unroll") for (int q = 0; q < kQ; ++q)                                          \
+        _Pragma("unroll") for (int t = 0; t < 2; ++t)                                         \
+          acc[t][q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[s & 1][q], bv[s & 1][t],      \
+                                                             acc[t][q], 0, 0, 0);             \
+      if (s + 1 < 8) {                                                                        \
+        _Pragma("unroll") for (int t = 0; t < 2; ++t)                                         \
+          bv[(s + 1) & 1][t] = decode_finish(fd[(s + 1) & 1][t]);                             \
       }                                                                                       \
       __builtin_amdgcn_sched_barrier(0);                                                      \
     }                                                                                         \
-    SAGE_PF_STAGE((gg + 1) & 1)                                                               \
-    __syncthreads();                                                                          \
+    asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");                             \
   }
   // the group count is rounded up to a multiple of three: groups past the last read zeros
   // (out-of-range loads) and add nothing, which keeps the loop free of exits that would
@@ -511,7 +658,6 @@ __device__ void prefill_body(const PrefillArgs& A, uint8_t* smem) {
     SAGE_PF_GROUP(2)
   }
 #undef SAGE_PF_GROUP
-#undef SAGE_PF_STAGE
 #undef SAGE_PF_X
 #undef SAGE_PF_WORDS
 
@@ -564,7 +710,7 @@ __device__ void prefill_body(const PrefillArgs& A, uint8_t* smem) {
 // registers, which lets two waves share a SIMD (two workgroups per compute unit when the LDS
 // allows).
 template <int L, int kQ>
-__global__ void __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(kQ == 4 ? 2 : 1, 2)))
+__global__ void __launch_bounds__(kPfThreads)
 prefill_kernel(PrefillArgs A) {
   extern __shared__ __align__(16) uint8_t smem[];
   prefill_body<L, kQ>(A, smem);
@@ -779,9 +925,21 @@ int sage_gemm_small(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, u
   if (xp_bytes) {
     // reorder the activations once, then every workgroup reads contiguous 16-byte chunks
     uint16_t* Xp = reinterpret_cast<uint16_t*>(wsb);
-    const int64_t n = (int64_t)M * A.d_in;
-    hipLaunchKernelGGL(permute_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, hs,
-                       X, (int64_t)ldx, m->pi, A.d_in, M, Xp);
+    const PermPlan pp = permute_plan(A.d_in, M, aligned(X, 16) && (ldx % 8) == 0);
+    if (pp.rows > 0) {
+      const dim3 grid((unsigned)ceil_div(M, pp.rows), (unsigned)pp.ranges);
+      const size_t lds = (size_t)pp.rows * A.d_in * 2;
+      const int64_t lx = ldx;
+      switch (pp.rows) {
+        case 8: hipLaunchKernelGGL(permute_rows_kernel<8>, grid, dim3(256), lds, hs, X, lx, m->pi, A.d_in, M, pp.units, Xp); break;
+        case 4: hipLaunchKernelGGL(permute_rows_kernel<4>, grid, dim3(256), lds, hs, X, lx, m->pi, A.d_in, M, pp.units, Xp); break;
+        case 2: hipLaunchKernelGGL(permute_rows_kernel<2>, grid, dim3(256), lds, hs, X, lx, m->pi, A.d_in, M, pp.units, Xp); break;
+        default: hipLaunchKernelGGL(permute_rows_kernel<1>, grid, dim3(256), lds, hs, X, lx, m->pi, A.d_in, M, pp.units, Xp); break;
+      }
+    } else {
+      hipLaunchKernelGGL(permute_gather_kernel, dim3((unsigned)M, (unsigned)ceil_div(A.d_in, 256)),
+                         dim3(256), 0, hs, X, (int64_t)ldx, m->pi, A.d_in, M, Xp);
+    }
     if (pf.kq) {
       PrefillArgs P{};
       P.packed = A.packed;

@@ -481,6 +481,25 @@ def test_gemm_prefill_split(d_out, d_in, M, K, V, ldy):
     check_gemm(f"split {d_out}x{d_in} K={K} M={M}", c, X, torch.from_numpy(np.ascontiguousarray(Y)))
 
 
+@pytest.mark.parametrize("d_out,d_in,M,identity", [(70, 33792, 9, False), (130, 1152, 130, True),
+                                                   (64, 1024, 1030, False)])
+def test_gemm_activation_reorder(d_out, d_in, M, identity):
+    """The activation reorder before the GEMM: a row too wide to stage in LDS (element-wise
+    gather), pi = NULL on the prefill path, and many rows per reorder workgroup."""
+    import dataclasses
+    import torch
+    rng = W.rng_for(147, d_in, M)
+    c = W.draw_codes(rng, d_out, d_in, 64, 4)
+    if identity:
+        c.pi = np.arange(d_in, dtype=np.int32)
+    X = W.draw_x(rng, (M, d_in))
+    p = upload_pack(c)
+    if identity:
+        p = dataclasses.replace(p, pi=None)
+    Y = sage.gemm_small(p, torch.from_numpy(X).cuda())
+    check_gemm(f"reorder {d_out}x{d_in} M={M} identity={identity}", c, X, Y)
+
+
 def test_gemm_strided_rows():
     import torch
     c = W.draw_codes(W.rng_for(141), 200, 512, 32, 5)
