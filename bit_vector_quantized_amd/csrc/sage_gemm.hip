@@ -526,11 +526,13 @@ __device__ void prefill_body(const PrefillArgs& A, uint8_t* smem) {
   const int lane = tid & 63;
   const int h = lane >> 5;                    // k half of the 16-channel step
   const int r0 = lane & 31;                   // rows r0 and 32 + r0 of the tile
-  // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2). Renumber them so
-  // that each XCD takes a contiguous run of (tile quad, row block, split) in tile-quad-fastest
-  // order: the workgroups that read one activation slab then share an L2 (measured 2-6 % faster).
-  int bx, by, bz;  // tile quad, row block, split
-  {
+  // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2). Without splits,
+  // renumber them so that each XCD takes a contiguous run of (tile quad, row block) in
+  // tile-quad-fastest order: the workgroups that read one activation slab then share an L2
+  // (measured 1-6 % faster). With splits the plain order is kept: on 2560x9728 at M = 128
+  // (19 splits) the renumbered grid ran 33 us against 24 us.
+  int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;  // tile quad, row block, split
+  if (gridDim.z == 1) {
     const int n = gridDim.x * gridDim.y * gridDim.z;
     const int lid = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
     const int xcd = lid & 7, k = lid >> 3, base = n >> 3, rem = n & 7;
@@ -747,14 +749,15 @@ PrefillFn prefill_fn(int L, int kq) {
   }
 }
 
-// Split sums of the prefill kernel, one output per thread: thread i reads element i of every
-// split's plane (laid out as the kernel's accumulators, 64 x rows floats per wave tile and block)
-// and writes Y[m][n] = fp16(partial[0] + ... + partial[S-1]), added in split order.
+// Split sums of the prefill kernel, four outputs per thread: thread j reads elements 4j .. 4j + 3
+// of every split's plane (laid out as the kernel's accumulators, 64 x rows floats per wave tile
+// and block; the four are lanes l .. l + 3 of one accumulator, i.e. four consecutive outputs of
+// one row) and writes Y[m][n] = fp16(partial[0] + ... + partial[S-1]), added in split order.
 __global__ void __launch_bounds__(256) prefill_reduce_kernel(const float* __restrict__ partial,
                                                              int S, int64_t plane, int rows,
                                                              int rt, int M, int d_out,
                                                              uint16_t* __restrict__ Y, int64_t ldy) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= plane) return;
   const int tile = 64 * rows;                 // floats of one wave tile and activation block
   const int64_t c = i / tile;
@@ -769,9 +772,32 @@ __global__ void __launch_bounds__(256) prefill_reduce_kernel(const float* __rest
   const int n = r * kTileRows + t * 32 + (lane & 31);
   const int m = b * rows + q * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
   if (m >= M || n >= d_out) return;
-  float sum = partial[i];
-  for (int sp = 1; sp < S; ++sp) sum += partial[sp * plane + i];
-  Y[(int64_t)m * ldy + n] = f2h(sum);
+  const float4* p4 = reinterpret_cast<const float4*>(partial + i);
+  const int64_t step = plane / 4;
+  float4 sum = p4[0];
+  int sp = 1;
+  for (; sp + 8 <= S; sp += 8) {
+    // eight splits' loads in flight, added in split order
+    float4 a[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a[k] = p4[(sp + k) * step];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      sum.x += a[k].x;
+      sum.y += a[k].y;
+      sum.z += a[k].z;
+      sum.w += a[k].w;
+    }
+  }
+  for (; sp < S; ++sp) {
+    const float4 a0 = p4[sp * step];
+    sum.x += a0.x; sum.y += a0.y; sum.z += a0.z; sum.w += a0.w;
+  }
+  uint16_t* y = Y + (int64_t)m * ldy + n;
+  y[0] = f2h(sum.x);
+  if (n + 1 < d_out) y[1] = f2h(sum.y);
+  if (n + 2 < d_out) y[2] = f2h(sum.z);
+  if (n + 3 < d_out) y[3] = f2h(sum.w);
 }
 
 // Launch shape of the prefill kernel: kq 32-row activation blocks per workgroup, S column splits
@@ -979,7 +1005,7 @@ int sage_gemm_small(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, u
       hipLaunchKernelGGL(fn, grid, dim3(kPfThreads), prefill_lds(A.L, pf.kq), hs, P);
       if (pf.S > 1) {
         const int64_t plane = prefill_plane(pf, A.d_out, M);
-        hipLaunchKernelGGL(prefill_reduce_kernel, dim3((unsigned)((plane + 255) / 256)), dim3(256),
+        hipLaunchKernelGGL(prefill_reduce_kernel, dim3((unsigned)((plane / 4 + 255) / 256)), dim3(256),
                            0, hs, P.partial, pf.S, plane, 32 * pf.kq, A.rt, M, A.d_out, Y,
                            (int64_t)ldy);
       }
