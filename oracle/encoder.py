@@ -8,6 +8,12 @@ Written from "SAGE: Pushing 2-Bit Vector-Quantized LLMs toward Real-World Usabil
   position_weights    §3.2, Eq. (4): omega_i = e_{a_i}^gamma divided by the subvector's mean of
                       e^gamma, so the eight weights average to one.
   assign              §3.2, Eq. (6): weighted closed-form radius and argmax of the substituted score.
+  assign_ordered      the same, with every 8-term sum taken left to right (i = 0..7) and no fused
+                      operations, so that a second implementation can reproduce each rounding and
+                      therefore each argmax decision exactly.
+  encode_fields       §3.2 Eq. (6) with §3.1 Eq. (2) / Appendix A.6 Eq. (14): the final assignment
+                      and radius grid of one matrix for a given fp16 codebook, permutation and
+                      position weights (no codebook fit), built on assign_ordered.
   kmeans              §3.2 + §4.1: activation-weighted spherical k-means (20 iterations on up to
                       65,536 sampled subvectors by default).
   radius_grid         §3.1 Eq. (2) with Appendix A.6 Eq. (14): per 128-weight group, offset = min
@@ -38,6 +44,9 @@ Readings where the paper is silent (each one also listed in the design notes):
 Parity status:
   channel_energy, esg_permutation, position_weights, assign, radius_grid, abs_score: pinned by the
     CPU tests (worked example of Eq. (5), closed forms, brute-force minimisation, special cases).
+  assign_ordered: pinned bit for bit by a pure-Python loop over the same operations, and against
+    assign (same decisions away from near-ties, radii within a few ulps).
+  encode_fields: pinned by exact recovery of planted matrices for a given codebook.
   kmeans: PARITY UNPINNED. The paper gives neither its initialisation nor its update rule, so only
     invariants are checked (nonnegative unit codewords, non-increasing objective, planted fixed
     point).
@@ -124,6 +133,37 @@ def assign(P: np.ndarray, omega: np.ndarray, C: np.ndarray,
         rr[ok] = nz[ok] / dz[ok]
         z[s:s + chunk] = zz
         r[s:s + chunk] = rr
+    return z, r
+
+
+def assign_ordered(P: np.ndarray, omega: np.ndarray, C: np.ndarray,
+                   chunk: int = 4096) -> Tuple[np.ndarray, np.ndarray]:
+    """Eq. (6) like `assign`, with a fixed evaluation order: t_i = w_i p_i; num_k = t_0 c_k0, then
+    num_k = num_k + t_i c_ki for i = 1..7; den_k likewise from w_i (c_ki c_ki); score_k =
+    (num_k num_k) / den_k (0 where den_k is 0); z = first maximum; r = num_z / den_z (0 where
+    den_z is 0). Every step is one IEEE double operation (numpy element-wise ops do not fuse)."""
+    P = np.asarray(P, dtype=np.float64)
+    W = np.asarray(omega, dtype=np.float64)
+    C = np.asarray(C, dtype=np.float64)
+    C2 = C * C
+    n, v = P.shape
+    z = np.empty(n, dtype=np.int64)
+    r = np.empty(n, dtype=np.float64)
+    for s in range(0, n, chunk):
+        t = W[s:s + chunk] * P[s:s + chunk]
+        w = W[s:s + chunk]
+        num = t[:, 0:1] * C[None, :, 0]
+        den = w[:, 0:1] * C2[None, :, 0]
+        for i in range(1, v):
+            num = num + t[:, i:i + 1] * C[None, :, i]
+            den = den + w[:, i:i + 1] * C2[None, :, i]
+        pos = den > 0
+        score = np.where(pos, (num * num) / np.where(pos, den, 1.0), 0.0)
+        zz = np.argmax(score, axis=1)
+        rows = np.arange(zz.size)
+        nz, dz = num[rows, zz], den[rows, zz]
+        z[s:s + chunk] = zz
+        r[s:s + chunk] = np.where(dz > 0, nz / np.where(dz > 0, dz, 1.0), 0.0)
     return z, r
 
 
@@ -272,6 +312,40 @@ def encode_matrix(W: np.ndarray, e: Optional[np.ndarray], K: int, V: int, gamma:
         "K": K, "V": V, "d_out": d_out, "d_in": d_in,
         "_r_tilde": r.reshape(d_out, m), "_kmeans_history": np.asarray(hist),
         "_codebook64": C64,
+    }
+
+
+def encode_fields(W: np.ndarray, pi: np.ndarray, omega: np.ndarray, codebook16: np.ndarray,
+                  V: int) -> Dict[str, np.ndarray]:
+    """The stored fields of W [d_out, d_in] (original column order) for a given fp16 codebook
+    [K, 8] (uint16 bits or float16 values), permutation pi (gather form) and position weights
+    omega [d_in] in permuted order: signs, idx = z and rcode = q from Eq. (6) evaluated with
+    `assign_ordered` on the fp16 codebook, then the per-group fp16 grid of Eq. (2) / Eq. (14)."""
+    W = np.asarray(W, dtype=np.float64)
+    d_out, d_in = W.shape
+    if d_in % G_WEIGHTS:
+        raise ValueError("d_in must be a multiple of 128")
+    C16 = np.asarray(codebook16)
+    C16 = C16.view(np.float16) if C16.dtype == np.uint16 else C16.astype(np.float16)
+    C = C16.astype(np.float64).reshape(-1, V_SUB)
+    pi = np.asarray(pi, dtype=np.int64)
+    m = d_in // V_SUB
+    Wsub = W[:, pi].reshape(d_out, m, V_SUB)
+    P = np.abs(Wsub).reshape(-1, V_SUB)
+    om = np.broadcast_to(np.asarray(omega, dtype=np.float64).reshape(1, m, V_SUB),
+                         (d_out, m, V_SUB)).reshape(-1, V_SUB)
+    z, r = assign_ordered(P, om, C)
+    mu, delta, q = radius_grid(r.reshape(d_out, m), V)
+    return {
+        "signs": sign_bytes(Wsub),
+        "idx": z.reshape(d_out, m).astype(np.uint8),
+        "rcode": q.astype(np.uint8),
+        "mu": mu.astype(np.float16).view(np.uint16),
+        "delta": delta.astype(np.float16).view(np.uint16),
+        "codebook": C16.reshape(-1, V_SUB).view(np.uint16),
+        "pi": pi.astype(np.int32),
+        "K": C.shape[0], "V": V, "d_out": d_out, "d_in": d_in,
+        "_r_tilde": r.reshape(d_out, m),
     }
 
 

@@ -322,3 +322,97 @@ def test_single_matrix_calibration_encode():
     assert np.all(np.abs(np.linalg.norm(cb, axis=1) - 1.0) <= 2.0 ** -10)
     s = encoder.abs_score(cfg.W, decoder.decode(enc), e)
     assert 0.0 < s < 0.5
+
+
+# ------------------------------------------------------------------------------ fixed-order Eq. (6)
+
+def _assign_python(P, omega, C):
+    """Eq. (6) by plain Python float loops in the order assign_ordered states (left to right)."""
+    z_out, r_out = [], []
+    for p, w in zip(P.tolist(), omega.tolist()):
+        t = [w[i] * p[i] for i in range(8)]
+        best, bz, bnum, bden = None, 0, 0.0, 0.0
+        for k, c in enumerate(C.tolist()):
+            num = t[0] * c[0]
+            den = w[0] * (c[0] * c[0])
+            for i in range(1, 8):
+                num = num + t[i] * c[i]
+                den = den + w[i] * (c[i] * c[i])
+            score = (num * num) / den if den > 0 else 0.0
+            if best is None or score > best:
+                best, bz, bnum, bden = score, k, num, den
+        z_out.append(bz)
+        r_out.append(bnum / bden if bden > 0 else 0.0)
+    return np.array(z_out), np.array(r_out)
+
+
+def test_assign_ordered_matches_python_loop_bit_for_bit():
+    rng = np.random.default_rng(21)
+    n, K = 60, 16
+    P = np.abs(rng.standard_normal((n, 8)))
+    P[3] = 0.0                                   # zero subvector
+    omega = rng.lognormal(size=(n, 8))
+    omega[5, :4] = 0.0                           # weights that vanish on part of the subvector
+    C = np.abs(rng.standard_normal((K, 8)))
+    C /= np.linalg.norm(C, axis=1, keepdims=True)
+    C[2, 4:] = 0.0                               # a codeword with zero weighted norm for row 5
+    C = C.astype(np.float16).astype(np.float64)
+    omega[5, 4:] = rng.lognormal(size=4)
+    z, r = encoder.assign_ordered(P, omega, C)
+    zp, rp = _assign_python(P, omega, C)
+    assert np.array_equal(z, zp)
+    assert np.array_equal(r.view(np.uint64), rp.view(np.uint64))
+    assert z[3] == 0 and r[3] == 0.0
+
+
+def test_assign_ordered_agrees_with_assign():
+    rng = np.random.default_rng(22)
+    n, K = 20000, 64
+    P = np.abs(rng.standard_normal((n, 8)))
+    omega = rng.lognormal(size=(n, 8))
+    C = np.abs(rng.standard_normal((K, 8)))
+    C = (C / np.linalg.norm(C, axis=1, keepdims=True)).astype(np.float16).astype(np.float64)
+    z1, r1 = encoder.assign(P, omega, C)
+    z2, r2 = encoder.assign_ordered(P, omega, C)
+    num = (omega * P) @ C.T
+    den = omega @ (C * C).T
+    score = num * num / den
+    rows = np.arange(n)
+    differ = z1 != z2
+    # a different choice is only allowed between scores equal to rounding
+    assert np.all(np.abs(score[rows, z1] - score[rows, z2])[differ]
+                  <= 1e-12 * score[rows, z1][differ])
+    same = ~differ
+    assert np.all(np.abs(r1 - r2)[same] <= 1e-14 * np.abs(r1)[same])
+
+
+@pytest.mark.parametrize("K,V", [(16, 6), (64, 4), (256, 2)])
+def test_encode_fields_exact_recovery_planted(K, V):
+    rng = np.random.default_rng(K + 100)
+    d_out, d_in = 24, 384
+    e = rng.lognormal(size=d_in)
+    pi = encoder.esg_permutation(e)
+    W, parts = planted_matrix(d_out, d_in, K, V, pi, seed=K + V + 1)
+    omega = encoder.position_weights(e[pi], 0.75).reshape(-1)
+    enc = encoder.encode_fields(W, pi, omega, parts["C"].astype(np.float16), V)
+    assert np.array_equal(enc["idx"], parts["z"])
+    assert np.array_equal(enc["rcode"], parts["q"])
+    assert np.array_equal(enc["mu"].view(np.float16).astype(np.float64), parts["mu"])
+    assert np.array_equal(enc["delta"].view(np.float16).astype(np.float64), parts["delta"])
+    assert np.array_equal(decoder.decode(enc), W)          # bit-exact in float64
+    Wp = W[:, pi].reshape(d_out, -1, 8)
+    assert np.array_equal(enc["signs"], encoder.sign_bytes(Wp))
+
+
+def test_encode_fields_reproduces_encode_matrix_with_its_codebook():
+    """With the codebook, permutation and weights the full encoder produced, the fixed-codebook
+    encoder gives the same fields (the two differ only in the summation order of Eq. (6))."""
+    rng = np.random.default_rng(23)
+    d_out, d_in = 32, 256
+    W = rng.standard_normal((d_out, d_in)) * 0.02
+    e = rng.lognormal(size=d_in)
+    full = encoder.encode_matrix(W, e, 64, 4, gamma=0.75, iters=5, seed=4)
+    omega = encoder.position_weights(e[full["pi"]], 0.75).reshape(-1)
+    fixed = encoder.encode_fields(W, full["pi"], omega, full["codebook"], 4)
+    for key in ("signs", "idx", "rcode", "mu", "delta"):
+        assert np.array_equal(fixed[key], full[key]), key
