@@ -68,6 +68,11 @@ _SIGNATURES = {
     "sage_stream_read": (_I, [_P, _SZ, _P, _P]),
     "sage_mlp_workspace_bytes": (_I, [_PM, _PM, _PM, ctypes.POINTER(ctypes.c_size_t)]),
     "sage_mlp": (_I, [_PM, _PM, _PM, _P, _P, _P, _P, _SZ, _P]),
+    "sage_encode_fields": (_I, [_P, _I, _I, ctypes.c_int64, _P, _P, _P, _I, _I,
+                                _P, _P, _P, _P, _P, _P, _P]),
+    "sage_abs_score_workspace_bytes": (_I, [_I, _I, _PSZ]),
+    "sage_abs_score": (_I, [_P, _I, _I, ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P, _I, _I, _P,
+                            _P, _P, _SZ, _P]),
 }
 
 
@@ -185,6 +190,49 @@ def unpack(p: Packed, stream=None):
                                             _ptr(signs), _ptr(idx), _ptr(rcode), _ptr(mu),
                                             _ptr(delta), _stream(stream)))
     return signs, idx, rcode, mu, delta
+
+
+def encode_fields(W, pi, omega, codebook, log2K: int, V: int, overflow=None, stream=None):
+    """Code fields of W (fp32 [d_out, d_in], original order) for a given fp16 codebook [K, 8],
+    permutation (int32 [d_in] or None) and float64 position weights [d_in] in permuted order.
+    Returns (signs, idx, rcode, mu, delta) as device tensors in sage_pack's layout; `overflow`,
+    if given, is a uint32 device counter incremented for every group outside the fp16 range."""
+    torch = _torch()
+    _require_cuda(W, pi, omega, codebook, overflow)
+    d_out, d_in = W.shape
+    dev = W.device
+    m, ng = d_in // 8, d_in // 128
+    signs = torch.empty((d_out, m), dtype=torch.uint8, device=dev)
+    idx = torch.empty_like(signs)
+    rcode = torch.empty_like(signs)
+    mu = torch.empty((d_out, ng), dtype=torch.float16, device=dev)
+    delta = torch.empty_like(mu)
+    _check("sage_encode_fields",
+           lib().sage_encode_fields(_ptr(W), d_out, d_in, W.stride(0), _ptr(pi), _ptr(omega),
+                                    _ptr(codebook), log2K, V, _ptr(signs), _ptr(idx),
+                                    _ptr(rcode), _ptr(mu), _ptr(delta), _ptr(overflow),
+                                    _stream(stream)))
+    return signs, idx, rcode, mu, delta
+
+
+def abs_score(W, e, fields, codebook, log2K: int, V: int, pi, stream=None):
+    """Eq. (8) score of an encoding: a float64 device tensor [numerator, denominator, ratio].
+    `fields` is (signs, idx, rcode, mu, delta) as encode_fields returns them; e holds the float64
+    channel energies in original order."""
+    torch = _torch()
+    signs, idx, rcode, mu, delta = fields
+    _require_cuda(W, e, signs, idx, rcode, mu, delta, codebook, pi)
+    d_out, d_in = W.shape
+    n = ctypes.c_size_t(0)
+    _check("sage_abs_score_workspace_bytes",
+           lib().sage_abs_score_workspace_bytes(d_out, d_in, ctypes.byref(n)))
+    ws = torch.empty(max(n.value, 8), dtype=torch.uint8, device=W.device)
+    out = torch.empty(3, dtype=torch.float64, device=W.device)
+    _check("sage_abs_score",
+           lib().sage_abs_score(_ptr(W), d_out, d_in, W.stride(0), _ptr(e), _ptr(signs), _ptr(idx),
+                                _ptr(rcode), _ptr(mu), _ptr(delta), _ptr(codebook), log2K, V,
+                                _ptr(pi), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
 
 
 def dequant(p: Packed, out=None, stream=None):

@@ -216,6 +216,51 @@ int sage_mlp(const sage_matrix_t* gate, const sage_matrix_t* up, const sage_matr
  */
 int sage_stream_read(const void* p, size_t bytes, uint32_t* sink, sage_stream_t stream);
 
+/*
+ * sage_encode_fields: the code fields of a matrix for a GIVEN codebook, permutation and position
+ * weights (the encoder's final assignment; the codebook fit itself is not done here).
+ *   W        fp32 [d_out][ldw] row-major, original column order, 4-byte aligned (ldw >= d_in).
+ *   pi       int32 [d_in], gather form as in sage_matrix_t (NULL = identity), 16-byte aligned.
+ *   omega    float64 [d_in], the position weights of §3.2 Eq. (4) in permuted order (omega[8j+i]
+ *            weighs position i of column subvector j), 8-byte aligned.
+ *   codebook fp16 [K][8], K = 2^log2K; (log2K, V) as for every matrix.
+ *   signs, idx, rcode  uint8 [d_out][d_in/8] and mu, delta fp16 [d_out][d_in/128]: written in the
+ *            layout sage_pack reads.
+ *   overflow optional uint32 counter in device memory (NULL = none): incremented once for every
+ *            group whose fp16 mu or delta is not finite (weights beyond the fp16 range); the
+ *            caller clears it.
+ * For subvector j of row r, with w the weights W[r, pi[8j+i]] and p = |w|: the sign bits are
+ * w_i < 0 (bit i; a zero weight is positive), z is the first maximum over codewords k of
+ * (sum_i omega_i p_i c_ki)^2 / sum_i omega_i c_ki^2 (§3.2 Eq. (6); 0 where the denominator is 0)
+ * and the fitted radius r~ = num_z / den_z. Per 128-weight group, mu = min r~ and delta =
+ * (max r~ - mu) / (2^V - 1) (§3.1 Eq. (2), App. A.6 Eq. (14)) are rounded to fp16 and
+ * q = clip(rint((r~ - mu16) / delta16), 0, 2^V - 1), q = 0 where delta16 = 0. Everything is
+ * computed in float64, sums left to right (i = 0..7) without fused multiply-adds, so the result is
+ * reproducible bit for bit by any implementation that follows the same order.
+ */
+int sage_encode_fields(const float* W, int d_out, int d_in, int64_t ldw, const int32_t* pi,
+                       const double* omega, const uint16_t* codebook, int log2K, int V,
+                       uint8_t* signs, uint8_t* idx, uint8_t* rcode, uint16_t* mu, uint16_t* delta,
+                       uint32_t* overflow, sage_stream_t stream);
+
+/*
+ * sage_abs_score: the energy-weighted relative reconstruction error of one encoding, §3.3
+ * Eq. (8): sum_c e_c ||W[:,c] - W_hat[:,c]||^2 / sum_c e_c ||W[:,c]||^2, the score the Adaptive
+ * Bit Split minimises over candidate splits (Eq. (9)); W_hat is the float64 decode of the fields
+ * (mu + q delta) * (+-c_z) placed at original column pi[p].
+ *   W, ldw, pi, fields, codebook, log2K, V  as for sage_encode_fields (pi 4-byte aligned here).
+ *   e        float64 [d_in] channel energies in ORIGINAL column order, 8-byte aligned.
+ *   out      float64 [3] in device memory: numerator, denominator, ratio (0 if the denominator is 0).
+ *   ws       workspace of sage_abs_score_workspace_bytes() bytes, 8-byte aligned: per-workgroup
+ *            partial sums, added in a fixed order (the result does not depend on scheduling).
+ */
+int sage_abs_score_workspace_bytes(int d_out, int d_in, size_t* bytes);
+int sage_abs_score(const float* W, int d_out, int d_in, int64_t ldw, const double* e,
+                   const uint8_t* signs, const uint8_t* idx, const uint8_t* rcode,
+                   const uint16_t* mu, const uint16_t* delta, const uint16_t* codebook,
+                   int log2K, int V, const int32_t* pi, double* out, void* ws, size_t ws_bytes,
+                   sage_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

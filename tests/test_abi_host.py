@@ -124,3 +124,31 @@ def test_stream_read_validation(L):
     assert L.sage_stream_read(ctypes.c_void_p((1 << 21) + 8), 16, sink, None) == ALIGN
     assert L.sage_stream_read(ctypes.c_void_p(1 << 21), 24, sink, None) == ALIGN
     assert L.sage_stream_read(ctypes.c_void_p(1 << 21), 0, sink, None) == OK
+
+
+def test_encode_and_abs_validation(L):
+    a = ctypes.c_void_p(4096)
+    args = [a, 16, 256, 256, a, a, a, 6, 4, a, a, a, a, a, None, None]
+
+    def enc(**kw):
+        v = list(args)
+        names = ["W", "d_out", "d_in", "ldw", "pi", "omega", "codebook", "log2K", "V", "signs",
+                 "idx", "rcode", "mu", "delta", "overflow", "stream"]
+        for k, x in kw.items():
+            v[names.index(k)] = x
+        return L.sage_encode_fields(*v)
+
+    assert enc(W=None) == NULL and enc(omega=None) == NULL and enc(delta=None) == NULL
+    assert enc(d_in=200) == SHAPE and enc(d_out=0) == SHAPE and enc(ldw=255) == SHAPE
+    assert enc(log2K=6, V=5) == SPLIT and enc(log2K=9, V=1) == SPLIT
+    assert enc(W=ctypes.c_void_p(4098)) == ALIGN and enc(omega=ctypes.c_void_p(4100)) == ALIGN
+    assert enc(pi=ctypes.c_void_p(4104)) == ALIGN
+    n = ctypes.c_size_t(0)
+    assert L.sage_abs_score_workspace_bytes(16, 256, ctypes.byref(n)) == OK and n.value >= 16
+    assert L.sage_abs_score_workspace_bytes(16, 100, ctypes.byref(n)) == SHAPE
+    sargs = [a, 16, 256, 256, a, a, a, a, a, a, a, 6, 4, None, a, a, n.value, None]
+    assert L.sage_abs_score(*sargs[:14], None, *sargs[15:]) == NULL
+    assert L.sage_abs_score(*sargs[:15], None, *sargs[16:]) == WS
+    assert L.sage_abs_score(*sargs[:16], n.value - 1, None) == WS
+    assert L.sage_abs_score(*sargs[:11], 6, 5, *sargs[13:]) == SPLIT
+    assert L.sage_abs_score(*sargs[:4], ctypes.c_void_p(4100), *sargs[5:]) == ALIGN

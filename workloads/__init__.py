@@ -137,6 +137,14 @@ class SingleMatrixCalib:
     seed: int = BASE_SEED + 1
 
 
+def encoder_matrix(rng: np.random.Generator, d_out: int, d_in: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Encoder inputs: W ~ N(0, 0.02^2) as fp32 [d_out, d_in] and channel energies e = s^2 with
+    s ~ LogNormal(0, 1) per channel (the energy of x_c = z s_c, z ~ N(0, 1)), float64 [d_in]."""
+    Wm = (0.02 * rng.standard_normal((d_out, d_in))).astype(np.float32)
+    e = rng.lognormal(0.0, 1.0, size=d_in) ** 2
+    return Wm, e
+
+
 def single_matrix_calib(d_out: int = 256, d_in: int = 1024, tokens: int = 512,
                         n_hot: int = 8, seed: int = BASE_SEED + 1) -> SingleMatrixCalib:
     rng = rng_for(seed)
