@@ -17,7 +17,10 @@ with counters (profiles/), a plain streaming read of the same bytes as the refer
 the CPU oracle's rate on a bounded sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--fused]
-                  [--workload layer|sweep|gemm|prefill|moe|single|all]
+                  [--workload layer|sweep|gemm|prefill|moe|encode|single|all]
+
+The secondary workloads print one JSON line per case (not the headline line); `encode` times the
+fixed-codebook GPU encoder (sage_encode_fields) on 9728x2560 for three splits.
 """
 from __future__ import annotations
 
@@ -34,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16, published
+FP64_PEAK_TFLOPS = 78.6        # fp64, published
 MALL_BYTES = 256 << 20
 
 
@@ -47,7 +51,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="layer",
-                    choices=["layer", "sweep", "gemm", "prefill", "moe", "single", "all"])
+                    choices=["layer", "sweep", "gemm", "prefill", "moe", "encode", "single", "all"])
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fused", action="store_true",
@@ -428,6 +432,43 @@ def bench_single_products(kind, steps, warmup):
     return lines
 
 
+def bench_encode(steps, warmup):
+    """The fixed-codebook encoder on a 9728x2560 fp32 weight (synthetic: random permutation and
+    positive position weights). Cost per subvector: for each of the K codewords 16 multiplies and
+    14 adds (numerator and denominator of Eq. (6)), one square and one division, all float64."""
+    import numpy as np
+    import torch
+    import workloads as W
+    import bit_vector_quantized_amd as sage
+    d_out, d_in = 9728, 2560
+    rng = W.rng_for(160)
+    Wm, e = W.encoder_matrix(rng, d_out, d_in)
+    Wd = torch.from_numpy(Wm).cuda()
+    pi = torch.from_numpy(W.draw_perm(rng, d_in)).cuda()
+    om = torch.from_numpy(rng.lognormal(size=d_in)).cuda()
+    n_sub = d_out * d_in // 8
+    for K, V in ((16, 6), (64, 4), (256, 2)):
+        cb = torch.from_numpy(W.draw_codebook(rng, K)).cuda()
+        fn = lambda: sage.encode_fields(Wd, pi, om, cb, K.bit_length() - 1, V)
+        for _ in range(max(1, warmup // 10)):
+            fn()
+        torch.cuda.synchronize()
+        n = max(3, steps // 20)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        dt = e0.elapsed_time(e1) / 1e3 / n
+        flops = n_sub * (K * 32 + 8)
+        line = {"workload": f"encode_{d_out}x{d_in}_K{K}V{V}", "us_per_call": round(dt * 1e6, 1),
+                "subvectors_per_s": round(n_sub / dt), "fp64_tflops": round(flops / dt / 1e12, 2),
+                "pct_fp64_peak": round(100 * flops / dt / 1e12 / FP64_PEAK_TFLOPS, 1)}
+        print(json.dumps(line), flush=True)
+
+
 def bench_moe(steps, warmup):
     import numpy as np
     import torch
@@ -501,6 +542,8 @@ def main():
         bench_single_products(args.workload, args.steps, args.warmup)
     if args.workload in ("moe", "all"):
         bench_moe(args.steps, args.warmup)
+    if args.workload in ("encode", "all"):
+        bench_encode(args.steps, args.warmup)
     if args.workload != "layer":
         return
 
