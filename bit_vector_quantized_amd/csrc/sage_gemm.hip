@@ -179,11 +179,12 @@ __global__ void __launch_bounds__(256) permute_gather_kernel(const uint16_t* __r
                                                              const int32_t* __restrict__ pi,
                                                              int d_in, int M,
                                                              uint16_t* __restrict__ Xp) {
-  const int m = blockIdx.x;
-  const int p = blockIdx.y * 256 + threadIdx.x;
+  // consecutive workgroups cover consecutive columns of one row (the gather stays inside a row)
+  const int p = blockIdx.x * 256 + threadIdx.x;
   if (p >= d_in) return;
   const int src = pi ? (int)min((uint32_t)pi[p], (uint32_t)d_in - 1u) : p;
-  Xp[(int64_t)m * d_in + p] = X[(int64_t)m * ldx + src];
+  for (int m = blockIdx.y; m < M; m += gridDim.y)
+    Xp[(int64_t)m * d_in + p] = X[(int64_t)m * ldx + src];
 }
 
 __device__ inline uint32_t mul_pair(uint32_t c, half2_t r) {
@@ -740,6 +741,15 @@ PrefillFn prefill_fn(int L, int kq) {
       default: return prefill_kernel<6, 8>;
     }
   }
+  if (kq == 2) {
+    switch (L) {
+      case 4: return prefill_kernel<4, 2>;
+      case 5: return prefill_kernel<5, 2>;
+      case 6: return prefill_kernel<6, 2>;
+      case 7: return prefill_kernel<7, 2>;
+      default: return prefill_kernel<8, 2>;
+    }
+  }
   switch (L) {
     case 4: return prefill_kernel<4, 4>;
     case 5: return prefill_kernel<5, 4>;
@@ -810,7 +820,7 @@ struct PfPlan {
 
 size_t prefill_lds(int L, int kq) {
   return prefill_slab_offset(L) +
-         2 * (size_t)(kq == 8 ? PfShape<8>::kSlab : PfShape<4>::kSlab);
+         2 * (size_t)(kq == 8 ? PfShape<8>::kSlab : (kq == 4 ? PfShape<4>::kSlab : PfShape<2>::kSlab));
 }
 
 // From kPrefillMinRows rows on (measured on 9728x2560 and 2560x9728, M = 128 ... 1024, every
@@ -823,12 +833,25 @@ size_t prefill_lds(int L, int kq) {
 //    per output and split.
 //  - Below 256 rows the small-batch kernel wins unless the split is deep (grid of 128-row blocks
 //    at most an eighth of the compute units).
+//  - From 65 to 127 rows the same holds for kq = 2 (64-row blocks): 2560x9728 at M = 96 ran
+//    32 us split 12 ways against 39 us in the small-batch kernel; at M = 32 and 64, and on
+//    9728x2560, the small-batch kernel was faster.
 PfPlan prefill_plan(int L, int d_out, int d_in, int M) {
   PfPlan P;
-  if (M < kPrefillMinRows) return P;
   const int64_t cus = device_cu_count();
   const int ng = d_in / kGroupCols;
   const int64_t wx = ceil_div(ceil_div(d_out, kTileRows), kPfWaves);
+  if (M < kPrefillMinRows) {
+    const int64_t wgs2 = wx * ceil_div(M, PfShape<2>::kRows);
+    if (M <= PfShape<2>::kRows || 8 * wgs2 > cus) return P;
+    int64_t S = cus / wgs2;
+    if (S > ng / 2) S = ng / 2;
+    if (S < 1) S = 1;
+    P.kq = 2;
+    P.gs = ceil_div(ng, (int)S);
+    P.S = ceil_div(ng, P.gs);
+    return P;
+  }
   const int64_t wgs8 = wx * ceil_div(M, PfShape<8>::kRows);
   if (M > PfShape<4>::kRows && prefill_lds(L, 8) <= 160 * 1024 && 2 * wgs8 >= cus) {
     P.kq = 8;
@@ -974,7 +997,8 @@ int sage_gemm_small(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, u
         default: hipLaunchKernelGGL(permute_rows_kernel<1>, grid, dim3(256), lds, hs, X, lx, m->pi, A.d_in, M, pp.units, Xp); break;
       }
     } else {
-      hipLaunchKernelGGL(permute_gather_kernel, dim3((unsigned)M, (unsigned)ceil_div(A.d_in, 256)),
+      hipLaunchKernelGGL(permute_gather_kernel,
+                         dim3((unsigned)ceil_div(A.d_in, 256), (unsigned)std::min(M, 65535)),
                          dim3(256), 0, hs, X, (int64_t)ldx, m->pi, A.d_in, M, Xp);
     }
     if (pf.kq) {
@@ -994,11 +1018,12 @@ int sage_gemm_small(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, u
       P.gs = pf.gs;
       if (pf.S > 1) P.partial = reinterpret_cast<float*>(wsb + xp_bytes);
       const PrefillFn fn = prefill_fn(A.L, pf.kq);
-      static bool attr_set[2][9] = {};
-      if (!attr_set[pf.kq == 8][A.L]) {
+      static bool attr_set[3][9] = {};
+      const int kqi = pf.kq == 8 ? 2 : (pf.kq == 4 ? 1 : 0);
+      if (!attr_set[kqi][A.L]) {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        attr_set[pf.kq == 8][A.L] = true;
+        attr_set[kqi][A.L] = true;
       }
       const dim3 grid((unsigned)ceil_div(A.rt, kPfWaves), (unsigned)ceil_div(M, 32 * pf.kq),
                       (unsigned)pf.S);

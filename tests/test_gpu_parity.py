@@ -459,10 +459,11 @@ def test_gemm_prefill_kernel(d_out, d_in, M, K, V):
 
 
 @pytest.mark.parametrize("d_out,d_in,M,K,V,ldy", [(130, 1408, 130, 32, 5, 130), (130, 1280, 300, 256, 2, 136),
-                                                   (640, 9728, 128, 16, 6, 640), (200, 2432, 257, 64, 4, 203)])
+                                                   (640, 9728, 128, 16, 6, 640), (200, 2432, 257, 64, 4, 203),
+                                                   (640, 9728, 96, 64, 4, 640), (200, 2432, 100, 256, 2, 203)])
 def test_gemm_prefill_split(d_out, d_in, M, K, V, ldy):
     """Grids too narrow for the compute units: the prefill kernel splits the column groups
-    (ragged last split, 128- and 256-row activation blocks, output rows wider than d_out) and a
+    (ragged last split, 64-, 128- and 256-row activation blocks, output rows wider than d_out) and a
     second kernel adds the splits; a repeated call gives the same bits."""
     import torch
     rng = W.rng_for(146, d_out, d_in, M)
