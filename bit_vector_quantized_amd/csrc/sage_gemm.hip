@@ -463,10 +463,11 @@ typedef float float16_t __attribute__((ext_vector_type(16)));
 struct PrefillArgs {
   const uint8_t* packed;
   const uint16_t* codebook;
-  const uint16_t* Xp;   // activations in permuted order, [M][d_in]
+  const uint16_t* Xp;   // activations in permuted order, [M][ldx], 16-byte aligned rows
   uint16_t* Y;
   float* partial;       // split-K partial sums, see the split store below (S > 1)
   int64_t ldy;
+  int64_t ldx;          // elements between activation rows (a multiple of 8)
   int32_t d_out, d_in, M, L;
   int32_t rt, ng;
   int32_t S, gs;        // column splits (blockIdx.z) and groups per split
@@ -559,13 +560,13 @@ __device__ void prefill_body(const PrefillArgs& A, uint8_t* smem) {
       view(A.packed + ((int64_t)rt * A.ng + g0) * kBlockBytes,
            tile_ok ? (uint32_t)(ng * kBlockBytes) : 0u);
   const __amdgpu_buffer_rsrc_t x_rs =
-      view(A.Xp + (int64_t)m0 * A.d_in + g0 * kGroupCols,
-           (uint32_t)((mrows * A.d_in - g0 * kGroupCols) * 2));
+      view(A.Xp + m0 * A.ldx + g0 * kGroupCols,
+           (uint32_t)(((int64_t)(mrows - 1) * A.ldx + A.d_in - g0 * kGroupCols) * 2));
   // per-lane byte offsets, fixed for the whole loop; the group adds a uniform amount
   const uint32_t wa0 = kPlaneA + r0 * 16, wb0 = kPlaneB + r0 * 16, ws0 = kSidePlane + r0 * 8;
   // Buffer-to-LDS loads: lane l of a 1 KiB load j writes slot l % 16 of slab row 4 j + l / 16,
   // so it fetches chunk (l % 16) ^ ((4 j + l / 16) % 16) of that row; the chunk depends on j % 4.
-  const uint32_t row_bytes = (uint32_t)A.d_in * 2u;
+  const uint32_t row_bytes = (uint32_t)A.ldx * 2u;
   uint32_t xl[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
@@ -982,11 +983,18 @@ int sage_gemm_small(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, u
         wsb + xp_bytes + (size_t)A.mchunks * A.S * A.mrows_chunk * A.rt * kTileRows * 4);
   }
   hipStream_t hs = (hipStream_t)stream;
-  if (xp_bytes) {
+  // Activations already in stored column order (pi = NULL) with 16-byte aligned rows are read in
+  // place (a producer that writes its output permuted saves the reorder launch).
+  const bool direct = m->pi == nullptr && aligned(X, 16) && (ldx % 8) == 0;
+  const uint16_t* Xs = X;
+  int64_t xs_ld = ldx;
+  if (xp_bytes || direct) {
     // reorder the activations once, then every workgroup reads contiguous 16-byte chunks
     uint16_t* Xp = reinterpret_cast<uint16_t*>(wsb);
     const PermPlan pp = permute_plan(A.d_in, M, aligned(X, 16) && (ldx % 8) == 0);
-    if (pp.rows > 0) {
+    if (direct) {
+      // nothing to reorder
+    } else if (pp.rows > 0) {
       const dim3 grid((unsigned)ceil_div(M, pp.rows), (unsigned)pp.ranges);
       const size_t lds = (size_t)pp.rows * A.d_in * 2;
       const int64_t lx = ldx;
@@ -1001,11 +1009,16 @@ int sage_gemm_small(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, u
                          dim3((unsigned)ceil_div(A.d_in, 256), (unsigned)std::min(M, 65535)),
                          dim3(256), 0, hs, X, (int64_t)ldx, m->pi, A.d_in, M, Xp);
     }
+    if (!direct) {
+      Xs = Xp;
+      xs_ld = A.d_in;
+    }
     if (pf.kq) {
       PrefillArgs P{};
       P.packed = A.packed;
       P.codebook = A.codebook;
-      P.Xp = Xp;
+      P.Xp = Xs;
+      P.ldx = xs_ld;
       P.Y = Y;
       P.ldy = ldy;
       P.d_out = A.d_out;
@@ -1036,12 +1049,12 @@ int sage_gemm_small(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, u
       }
       return hip_status();
     }
-    A.X = Xp;
-    A.ldx = A.d_in;
+    A.X = Xs;
+    A.ldx = xs_ld;
     A.pi = nullptr;
     A.vec_x = 1;
   } else {
-    A.vec_x = (A.pi == nullptr && aligned(X, 16) && (ldx % 8) == 0) ? 1 : 0;
+    A.vec_x = 0;  // fewer than kPermuteMinRows rows, gathered through pi by the kernel
   }
   const int nt = tiles_for(M);
   const size_t lds = lds_for(A.L, nt, A.gs);

@@ -141,11 +141,15 @@ int sage_gemv_multi(const sage_matrix_t* mats, const uint16_t* const* xs, uint16
  * §3.5 and App. A.1, where each decoded weight is reused across the rows).
  *   X   fp16 [M][ldx] row-major, original channel order, ldx >= d_in, ldx even, 4-byte aligned.
  *   Y   fp16 [M][ldy] row-major, ldy >= d_out.
- *   M   >= 1. M = 1 runs the batch-one kernel; up to a few hundred rows a small-batch kernel
- *       (one decode feeds 16-64 rows); prefill-sized batches whose grid fills the device run a
- *       kernel that decodes each weight once per 128 rows and loops over all column groups.
+ *   M   >= 1. M = 1 runs the batch-one kernel; up to about a hundred rows a small-batch kernel
+ *       (one decode feeds 16-64 rows); larger batches run the prefill kernel, which decodes each
+ *       weight once per 64, 128 or 256 rows and, on grids narrower than the device, splits the
+ *       column groups and adds the splits in a second kernel (deterministic order).
  *   ws  as for sage_gemv, size from sage_gemm_small_workspace_bytes(); from 8 rows on it also
- *       holds X in permuted column order (written by the call).
+ *       holds X in permuted column order (written by the call) and the split partial sums.
+ *       When the matrix has pi = NULL (X already in stored column order, e.g. written permuted
+ *       by its producer) and X is 16-byte aligned with ldx a multiple of 8, X is read in place
+ *       and no reorder runs.
  */
 int sage_gemm_small_workspace_bytes(const sage_matrix_t* m, int M, size_t* bytes);
 int sage_gemm_small(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, uint16_t* Y,

@@ -501,6 +501,24 @@ def test_gemm_activation_reorder(d_out, d_in, M, identity):
     check_gemm(f"reorder {d_out}x{d_in} M={M} identity={identity}", c, X, Y)
 
 
+@pytest.mark.parametrize("M", [9, 40, 96, 300])
+def test_gemm_pre_permuted_strided_input(M):
+    """pi = NULL and 16-byte aligned rows: the activations are read in place (no reorder), here
+    with a row stride wider than d_in, on the small-batch and the prefill paths."""
+    import dataclasses
+    import torch
+    rng = W.rng_for(148, M)
+    d_out, d_in = 200, 1152
+    c = W.draw_codes(rng, d_out, d_in, 64, 4)
+    c.pi = np.arange(d_in, dtype=np.int32)
+    X = W.draw_x(rng, (M, d_in))
+    Xbig = torch.zeros((M, d_in + 24), dtype=torch.float16, device="cuda")
+    Xbig[:, :d_in] = torch.from_numpy(X).cuda()
+    p = dataclasses.replace(upload_pack(c), pi=None)
+    Y = sage.gemm_small(p, Xbig[:, :d_in])
+    check_gemm(f"pre-permuted strided M={M}", c, X, Y)
+
+
 def test_gemm_strided_rows():
     import torch
     c = W.draw_codes(W.rng_for(141), 200, 512, 32, 5)
