@@ -15,6 +15,13 @@ Written from "SAGE: Pushing 2-Bit Vector-Quantized LLMs toward Real-World Usabil
                  paper quantizes these linear layers but does not define the block): the gate and
                  up products rounded to fp16, h = fp16(silu(gate) * up) with silu(t) = t/(1+e^-t),
                  then y = W_down h. Only this composition is new here; each product is gemv above.
+  rmsnorm_permute, silu_mul_permute
+                 the producers of §3.5's compiled decoding, which fuse each projection's input
+                 permutation into the preceding normalization or activation: out[:, p] =
+                 f(X)[:, pi[p]] for f = RMSNorm (x / sqrt(mean(x^2) + eps) times a weight gamma,
+                 the normalization of the decoder family evaluated; the paper does not define it)
+                 or f = silu(g) * u. Returned in float64, before the fp16 rounding a producer
+                 applies.
 
 Every step here is exact in float64: mu, delta and codeword entries are fp16 values, q has at most
 6 bits, so mu + q*delta and its product with a codeword entry need far fewer than 53 bits.
@@ -23,7 +30,9 @@ dequant_fp16 is therefore the correctly rounded fp16 of the exact decoded weight
 Parity status: pinned by the CPU tests (exact recovery of planted matrices, the equal-radii special
 case of Appendix A.6, unit-vector probes of the permutation direction and a brute-force loop
 matrix-vector product on tiny shapes; silu at closed-form points and the identity
-silu(t) - silu(-t) = t; the block's zero-gate and zero-up cases).
+silu(t) - silu(-t) = t; the block's zero-gate and zero-up cases; RMSNorm's unit root-mean-square
+output, scale invariance and a hand-worked vector; the producers' permutation as a column gather
+checked with unit probes).
 """
 from __future__ import annotations
 
@@ -131,3 +140,21 @@ def swiglu_mlp(gate: Any, up: Any, down: Any, x: np.ndarray):
     u16 = gemv(up, x).astype(np.float16).astype(np.float64)
     h = (silu(g16) * u16).astype(np.float16).astype(np.float64)
     return h, decode(down) @ h
+
+
+def rmsnorm_permute(X: np.ndarray, gamma: np.ndarray, eps: float, pi=None) -> np.ndarray:
+    """Rows of X [M, d] (or one vector [d]) normalised by their root mean square and scaled by
+    gamma [d], in original channel order; then column p of the result is column pi[p] of that
+    (pi None: identity). float64."""
+    X = np.asarray(X, np.float64)
+    g = np.asarray(gamma, np.float64)
+    ms = np.mean(X * X, axis=-1, keepdims=True)
+    Y = X / np.sqrt(ms + float(eps)) * g
+    return Y if pi is None else Y[..., np.asarray(pi, np.int64)]
+
+
+def silu_mul_permute(G: np.ndarray, U: np.ndarray, pi=None) -> np.ndarray:
+    """silu(G) * U element-wise (G, U: [M, d] or [d], fp16 values widened exactly), then column p of
+    the result is column pi[p] (pi None: identity). float64."""
+    Y = silu(G) * np.asarray(U, np.float64)
+    return Y if pi is None else Y[..., np.asarray(pi, np.int64)]

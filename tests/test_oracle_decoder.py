@@ -217,3 +217,39 @@ def test_swiglu_intermediate_is_fp16_and_follows_gate_sign():
     assert big.sum() > 10
     assert np.all(np.sign(h[big]) == np.sign(g[big]) * np.sign(u[big]))
     assert y.shape == (down.d_out,)
+
+
+# ------------------------------------------------------------------------------ producers (§3.5)
+
+def test_rmsnorm_unit_rms_scale_invariance_and_worked_vector():
+    rng = np.random.default_rng(31)
+    X = rng.standard_normal((5, 64)) * 3.0
+    ones = np.ones(64)
+    Y = decoder.rmsnorm_permute(X, ones, 0.0)
+    assert np.allclose(np.sqrt(np.mean(Y * Y, axis=1)), 1.0, rtol=1e-15, atol=0)
+    assert np.allclose(decoder.rmsnorm_permute(7.5 * X, ones, 0.0), Y, rtol=1e-14, atol=0)
+    # x = (3, 4, 0, 0): mean square 25/4, so x / 2.5; gamma doubles the second entry
+    y = decoder.rmsnorm_permute(np.array([3.0, 4.0, 0.0, 0.0]), np.array([1.0, 2.0, 1.0, 1.0]), 0.0)
+    assert np.array_equal(y, np.array([1.2, 3.2, 0.0, 0.0]))
+    # eps enters under the root: x = (1, 1), eps = 3 -> x / 2
+    assert np.array_equal(decoder.rmsnorm_permute(np.ones(2), np.ones(2), 3.0), np.full(2, 0.5))
+
+
+def test_producers_gather_through_pi():
+    """Column p of the permuted output is column pi[p] of the unpermuted one (unit probes)."""
+    rng = np.random.default_rng(32)
+    d = 16
+    pi = rng.permutation(d)
+    g = rng.lognormal(size=d)
+    for c in range(d):
+        x = np.zeros(d)
+        x[c] = 4.0
+        out = decoder.rmsnorm_permute(x, g, 0.0, pi)
+        p = int(np.nonzero(pi == c)[0][0])
+        assert np.nonzero(out)[0].tolist() == [p] and out[p] == 4.0 * g[c]
+        G = np.zeros(d)
+        G[c] = 2.0
+        U = np.full(d, 3.0)
+        h = decoder.silu_mul_permute(G, U, pi)
+        assert np.nonzero(h)[0].tolist() == [p]
+        assert h[p] == 3.0 * 2.0 / (1.0 + np.exp(-2.0))
