@@ -71,6 +71,9 @@ _SIGNATURES = {
     "sage_encode_fields": (_I, [_P, _I, _I, ctypes.c_int64, _P, _P, _P, _I, _I,
                                 _P, _P, _P, _P, _P, _P, _P]),
     "sage_abs_score_workspace_bytes": (_I, [_I, _I, _PSZ]),
+    "sage_rmsnorm_permute": (_I, [_P, _I, _I, ctypes.c_int64, _P, ctypes.c_float, _P, _P,
+                                  ctypes.c_int64, _P]),
+    "sage_silu_mul_permute": (_I, [_P, _P, _I, _I, ctypes.c_int64, _P, _P, ctypes.c_int64, _P]),
     "sage_abs_score": (_I, [_P, _I, _I, ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P, _I, _I, _P,
                             _P, _P, _SZ, _P]),
 }
@@ -232,6 +235,39 @@ def abs_score(W, e, fields, codebook, log2K: int, V: int, pi, stream=None):
            lib().sage_abs_score(_ptr(W), d_out, d_in, W.stride(0), _ptr(e), _ptr(signs), _ptr(idx),
                                 _ptr(rcode), _ptr(mu), _ptr(delta), _ptr(codebook), log2K, V,
                                 _ptr(pi), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def _rows(t):
+    return (1, t.shape[0], t.shape[0]) if t.dim() == 1 else (t.shape[0], t.shape[1], t.stride(0))
+
+
+def rmsnorm_permute(X, gamma, eps: float, pi=None, out=None, stream=None):
+    """fp16 RMSNorm of the rows of X ([M, d] or [d]) with weight gamma, written in the order of
+    pi (a matrix's permutation) or unpermuted when pi is None."""
+    torch = _torch()
+    _require_cuda(X, gamma, pi, out)
+    M, d, ld = _rows(X)
+    if out is None:
+        out = torch.empty(X.shape, dtype=torch.float16, device=X.device)
+    _check("sage_rmsnorm_permute",
+           lib().sage_rmsnorm_permute(_ptr(X), M, d, ld, _ptr(gamma), float(eps), _ptr(pi),
+                                      _ptr(out), _rows(out)[2], _stream(stream)))
+    return out
+
+
+def silu_mul_permute(G, U, pi=None, out=None, stream=None):
+    """fp16 silu(G) * U ([M, d] or [d], same strides), written in the order of pi."""
+    torch = _torch()
+    _require_cuda(G, U, pi, out)
+    M, d, ld = _rows(G)
+    if _rows(U)[2] != ld:
+        raise ValueError("G and U must share their row stride")
+    if out is None:
+        out = torch.empty(G.shape, dtype=torch.float16, device=G.device)
+    _check("sage_silu_mul_permute",
+           lib().sage_silu_mul_permute(_ptr(G), _ptr(U), M, d, ld, _ptr(pi), _ptr(out),
+                                       _rows(out)[2], _stream(stream)))
     return out
 
 

@@ -221,6 +221,29 @@ int sage_mlp(const sage_matrix_t* gate, const sage_matrix_t* up, const sage_matr
 int sage_stream_read(const void* p, size_t bytes, uint32_t* sink, sage_stream_t stream);
 
 /*
+ * Permuting producers (the compiled-decoding mode of §3.5: the next projection's input
+ * permutation is fused into the normalization or activation that produces its input). Their
+ * output is in the stored column order of a matrix whose pi is given here, so that matrix is then
+ * used with pi = NULL (its descriptor's pi set to NULL), which skips the gather in sage_gemv and
+ * the reorder in sage_gemm_small. pi NULL here gives the plain operation.
+ *   M rows (1 .. 65535) of d channels (d a multiple of 8); row m of an input starts at
+ *   element m*ld; row m of out at m*ldo (ld, ldo >= d). fp16 arrays 2-byte aligned (16-byte
+ *   aligned out with ldo % 8 == 0 gets vector stores), pi 4-byte aligned. out must not overlap
+ *   the inputs.
+ *
+ * sage_rmsnorm_permute: out[m][p] = fp16( X[m][c] / sqrt(mean_k X[m][k]^2 + eps) * gamma[c] ),
+ *   c = pi[p]; gamma fp16 [d] in original channel order; eps >= 0. The mean is over all d
+ *   channels, summed in fp32 in a fixed order; one rounding to fp16.
+ * sage_silu_mul_permute: out[m][p] = fp16( silu(G[m][c]) * U[m][c] ), c = pi[p],
+ *   silu(t) = t / (1 + e^-t); G and U share the row stride ld. fp32 arithmetic, one rounding.
+ */
+int sage_rmsnorm_permute(const uint16_t* X, int M, int d, int64_t ldx, const uint16_t* gamma,
+                         float eps, const int32_t* pi, uint16_t* out, int64_t ldo,
+                         sage_stream_t stream);
+int sage_silu_mul_permute(const uint16_t* G, const uint16_t* U, int M, int d, int64_t ld,
+                          const int32_t* pi, uint16_t* out, int64_t ldo, sage_stream_t stream);
+
+/*
  * sage_encode_fields: the code fields of a matrix for a GIVEN codebook, permutation and position
  * weights (the encoder's final assignment; the codebook fit itself is not done here).
  *   W        fp32 [d_out][ldw] row-major, original column order, 4-byte aligned (ldw >= d_in).

@@ -152,3 +152,17 @@ def test_encode_and_abs_validation(L):
     assert L.sage_abs_score(*sargs[:16], n.value - 1, None) == WS
     assert L.sage_abs_score(*sargs[:11], 6, 5, *sargs[13:]) == SPLIT
     assert L.sage_abs_score(*sargs[:4], ctypes.c_void_p(4100), *sargs[5:]) == ALIGN
+
+
+def test_producer_validation(L):
+    a = ctypes.c_void_p(4096)
+    assert L.sage_rmsnorm_permute(None, 1, 128, 128, a, 1e-6, None, a, 128, None) == NULL
+    assert L.sage_rmsnorm_permute(a, 0, 128, 128, a, 1e-6, None, a, 128, None) == SHAPE
+    assert L.sage_rmsnorm_permute(a, 1, 124, 128, a, 1e-6, None, a, 128, None) == SHAPE
+    assert L.sage_rmsnorm_permute(a, 1, 128, 127, a, 1e-6, None, a, 128, None) == SHAPE
+    assert L.sage_rmsnorm_permute(a, 1, 128, 128, a, -1.0, None, a, 128, None) == ARG
+    assert L.sage_rmsnorm_permute(ctypes.c_void_p(4097), 1, 128, 128, a, 1e-6, None, a, 128, None) == ALIGN
+    assert L.sage_rmsnorm_permute(a, 1, 128, 128, a, 1e-6, ctypes.c_void_p(4098), a, 128, None) == ALIGN
+    assert L.sage_silu_mul_permute(a, None, 1, 128, 128, None, a, 128, None) == NULL
+    assert L.sage_silu_mul_permute(a, a, 70000, 128, 128, None, a, 128, None) == SHAPE
+    assert L.sage_silu_mul_permute(a, a, 1, 128, 128, None, ctypes.c_void_p(4097), 128, None) == ALIGN
