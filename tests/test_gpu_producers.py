@@ -72,12 +72,14 @@ def test_silu_mul_permute(M, d, permuted):
     _check_ulp(f"silu*mul M={M} d={d} pi={permuted}", _bits(out), ref)
 
 
-def test_producers_strided_rows_and_scalar_stores():
-    """Input rows wider than d; output rows of odd stride (no vector stores)."""
+@pytest.mark.parametrize("pad", [40, 41])
+def test_producers_strided_rows_and_scalar_stores(pad):
+    """Input rows wider than d (16-byte aligned rows with pad 40, 2-byte aligned with 41); output
+    rows of odd stride (no vector stores)."""
     import torch
-    rng = W.rng_for(172)
+    rng = W.rng_for(172, pad)
     M, d = 4, 1024
-    Xw = W.draw_x(rng, (M, d + 40))
+    Xw = W.draw_x(rng, (M, d + pad))
     gamma = (1.0 + 0.1 * rng.standard_normal(d)).astype(np.float16)
     pi = W.draw_perm(rng, d)
     Xd = _dev(Xw)[:, :d]
