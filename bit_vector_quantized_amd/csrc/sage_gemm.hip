@@ -58,9 +58,12 @@ __device__ inline __amdgpu_buffer_rsrc_t view(const void* base, uint32_t bytes) 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
 
-// Sign masks of one nibble: bits 0/1 -> signs of the first fp16 pair, bits 2/3 -> second pair.
-__device__ inline uint2 nibble_masks(uint32_t n) {
-  return make_uint2(((n & 1u) << 15) | ((n & 2u) << 30), ((n & 4u) << 13) | ((n & 8u) << 28));
+// Sign masks of one nibble (n < 16): bits 0/1 -> sign bits 15/31 of the first fp16 pair, bits 2/3
+// -> sign bits 15/31 of the second pair. Two shifted copies of n OR-ed and masked put each bit in
+// place (three ALU operations a dword; measured faster than a 16-entry LDS table, which costs a
+// load a nibble against the LDS wait counter).
+__device__ inline uint2 sign_masks(uint32_t n) {
+  return make_uint2(((n << 15) | (n << 30)) & 0x80008000u, ((n << 13) | (n << 28)) & 0x80008000u);
 }
 
 // X[:, pi] for M rows into a dense [M][d_in] buffer (the reorder the paper does once per
@@ -192,7 +195,7 @@ __device__ inline uint32_t mul_pair(uint32_t c, half2_t r) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// LDS layout: codebook replicas [K][16][16 B], sign-mask table [16][8 B], flag, then the X tile
+// LDS layout: codebook replicas [K][16][16 B], 128 spare bytes, flag, then the X tile
 // [NT*16][gs*128 + 8] fp16 (also the part-sum exchange once the products are done).
 __host__ __device__ inline uint32_t gemm_xs_offset(int L) { return (1u << L) * 256u + 144u; }
 
@@ -222,7 +225,6 @@ __device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint
   const int xstride = A.gs * kGroupCols + 8;     // fp16 elements per staged activation row
 
   uint8_t* cb = smem;
-  uint2* smask = reinterpret_cast<uint2*>(smem + kK * 256);
   uint32_t* flag = reinterpret_cast<uint32_t*>(smem + kK * 256 + 128);
   _Float16* xs = reinterpret_cast<_Float16*>(smem + gemm_xs_offset(L));
 
@@ -276,7 +278,6 @@ __device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint
 #pragma unroll
     for (int r = 0; r < 16; ++r) *reinterpret_cast<u32x4*>(cb + tid * 256 + r * 16) = cw;
   }
-  if (tid < 16) smask[tid] = nibble_masks((uint32_t)tid);
   if constexpr (kVec) {
 #pragma unroll
     for (int i = 0; i < kVecLoads; ++i) {
@@ -321,8 +322,8 @@ __device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint
         const _Float16 rh = (_Float16)r;
         const half2_t r2 = half2_t{rh, rh};
         const uint4 c = *reinterpret_cast<const uint4*>(cb + z * 256 + laneoff);
-        const uint2 mlo = smask[s & 15u];
-        const uint2 mhi = smask[s >> 4];
+        const uint2 mlo = sign_masks(s & 15u);
+        const uint2 mhi = sign_masks(s >> 4);
         uint32_t w[4];
         w[0] = mul_pair(c.x ^ mlo.x, r2);
         w[1] = mul_pair(c.y ^ mlo.y, r2);
@@ -474,7 +475,7 @@ struct PrefillArgs {
 };
 
 __host__ __device__ inline uint32_t prefill_slab_offset(int L) {
-  return (1u << L) * 256u + 256u;  // after the codebook replicas and the sign-mask table
+  return (1u << L) * 256u + 256u;  // after the codebook replicas and 256 spare bytes
 }
 
 // One lane's packed words of one row in one group: payload dwords P0..P7, then X and G.
@@ -484,7 +485,7 @@ struct RowWords {
 };
 
 // First half of a subvector decode: the codeword replica, the two sign masks and the radius.
-// The LDS reads are only issued here; decode_finish consumes them a pipeline step later.
+// The codeword's LDS read is only issued here; decode_finish consumes it a pipeline step later.
 struct Fetched {
   uint4 c;
   uint2 mlo, mhi;
@@ -493,7 +494,7 @@ struct Fetched {
 
 template <int L>
 __device__ __forceinline__ Fetched decode_fetch(const RowWords& w, int s, int h, const uint8_t* cb,
-                                                const uint2* smask, uint32_t laneoff) {
+                                                uint32_t laneoff) {
   constexpr uint32_t kK = 1u << L;
   const uint32_t P = s < 4 ? w.a[s & 3] : w.b[s & 3];
   const uint32_t X = w.side[0], G = w.side[1];
@@ -506,8 +507,8 @@ __device__ __forceinline__ Fetched decode_fetch(const RowWords& w, int s, int h,
   Fetched o;
   o.r2 = half2_t{rh, rh};
   o.c = *reinterpret_cast<const uint4*>(cb + (f & (kK - 1u)) * 256 + laneoff);
-  o.mlo = smask[lo];
-  o.mhi = smask[hi];
+  o.mlo = sign_masks(lo);
+  o.mhi = sign_masks(hi);
   return o;
 }
 
@@ -550,7 +551,6 @@ __device__ void prefill_body(const PrefillArgs& A, uint8_t* smem) {
   const int g0 = bz * A.gs;                  // first column group of this split
   const int ng = min(A.ng - g0, A.gs);       // groups of this split
   uint8_t* cb = smem;
-  uint2* smask = reinterpret_cast<uint2*>(smem + kK * 256);
   uint8_t* slab0 = smem + prefill_slab_offset(L);
 
   const __amdgpu_buffer_rsrc_t cb_rs = view(A.codebook, kK * 16u);
@@ -608,7 +608,6 @@ __device__ void prefill_body(const PrefillArgs& A, uint8_t* smem) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) *reinterpret_cast<u32x4*>(cb + tid * 256 + r * 16) = cw;
   }
-  if (tid < 16) smask[tid] = nibble_masks((uint32_t)tid);
   // the first slab has landed once only the two word groups are outstanding
   asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
   __syncthreads();
@@ -637,8 +636,8 @@ __device__ void prefill_body(const PrefillArgs& A, uint8_t* smem) {
     half8_t bv[2][2];                                                                         \
     half8_t av[2][kQ];                                                                        \
     _Pragma("unroll") for (int t = 0; t < 2; ++t) {                                           \
-      fd[0][t] = decode_fetch<L>(wr[k][t], 0, h, cb, smask, laneoff);                         \
-      fd[1][t] = decode_fetch<L>(wr[k][t], 1, h, cb, smask, laneoff);                         \
+      fd[0][t] = decode_fetch<L>(wr[k][t], 0, h, cb, laneoff);                                \
+      fd[1][t] = decode_fetch<L>(wr[k][t], 1, h, cb, laneoff);                                \
     }                                                                                         \
     _Pragma("unroll") for (int q = 0; q < kQ; ++q)                                            \
       av[0][q] = *reinterpret_cast<const half8_t*>(abuf + q * 8192 + (a_hm ^ 0u));            \
@@ -652,7 +651,7 @@ __device__ void prefill_body(const PrefillArgs& A, uint8_t* smem) {
       }                                                                                       \
       if (s + 2 < 8) {                                                                        \
         _Pragma("unroll") for (int t = 0; t < 2; ++t)                                         \
-          fd[s & 1][t] = decode_fetch<L>(wr[k][t], s + 2, h, cb, smask, laneoff);             \
+          fd[s & 1][t] = decode_fetch<L>(wr[k][t], s + 2, h, cb, laneoff);                    \
       }                                                                                       \
       _Pragma("unroll") for (int q = 0; q < kQ; ++q)                                          \
         _Pragma("unroll") for (int t = 0; t < 2; ++t)                                         \
