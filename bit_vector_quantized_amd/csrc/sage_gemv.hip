@@ -92,10 +92,14 @@ struct SplitC {
 __host__ __device__ inline uint32_t lds_tail(int L, int gs) {
   return (L == 8) ? 98304u : (1u << L) * 256u + (uint32_t)gs * kSubPerGroup * 256u;
 }
-constexpr uint32_t kTailXp = 0;                                   // fp16 [gs * 128]
-constexpr uint32_t kTailRed = kMaxGroupsPerSplit * kGroupCols * 2;  // f32 [kParts-1][kTiles][64]
-constexpr uint32_t kTailFlag = kTailRed + (kParts - 1) * kTiles * 64 * 4;
-constexpr uint32_t kTailX = (kTailFlag + 16 + 255) / 256 * 256;     // fp16 [d_in], when staged
+// Offsets inside the tail for workgroup shape T (row tiles): gathered columns fp16 [max gs * 128],
+// part sums f32 [parts - 1][T][64], flag, whole x fp16 [d_in] when staged.
+constexpr uint32_t kTailXp = 0;
+__host__ __device__ constexpr uint32_t tail_red(int T) { return shape_max_gs(T) * kGroupCols * 2; }
+__host__ __device__ constexpr uint32_t tail_flag(int T) {
+  return tail_red(T) + (kWaves / T - 1) * T * 64 * 4;
+}
+__host__ __device__ constexpr uint32_t tail_x(int T) { return (tail_flag(T) + 16 + 255) / 256 * 256; }
 
 struct Resolved {
   const uint8_t* packed;
@@ -231,10 +235,13 @@ __device__ inline void mlp_input(const Job& J, uint16_t* xw, int tid) {
   }
 }
 
-template <int L, bool kWholeX, bool kFused>
+template <int L, int kT, bool kWholeX, bool kFused>
 __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int inst, int rq,
                                           int split, uint8_t* smem) {
   using C = SplitC<L>;
+  constexpr int kTiles = WgShape<kT>::kTiles;
+  constexpr int kParts = WgShape<kT>::kParts;
+  constexpr int kMaxUnits = WgShape<kT>::kMaxUnits;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: addresses in SGPRs
   const int lane = tid & 63;
@@ -252,8 +259,8 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int i
   const int cols = ngl * kGroupCols;
   const uint32_t tail = lds_tail(L, J.gs);
   uint16_t* xp = reinterpret_cast<uint16_t*>(smem + tail + kTailXp);
-  float* red = reinterpret_cast<float*>(smem + tail + kTailRed);
-  uint32_t* flag = reinterpret_cast<uint32_t*>(smem + tail + kTailFlag);
+  float* red = reinterpret_cast<float*>(smem + tail + tail_red(kT));
+  uint32_t* flag = reinterpret_cast<uint32_t*>(smem + tail + tail_flag(kT));
 
   // 1. Loads, in the order their data is needed.
   const __amdgpu_buffer_rsrc_t cb_rs = view(R.codebook, C::kK * 16u);
@@ -265,7 +272,12 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int i
   const __amdgpu_buffer_rsrc_t w_rs = view(blk0, tile_ok ? (uint32_t)(ngl * kBlockBytes) : 0u);
 
   const u32x4 cw = __builtin_amdgcn_raw_buffer_load_b128(cb_rs, tid * 16, 0, 0);
-  const uint32_t src = __builtin_amdgcn_raw_buffer_load_b32(pi_rs, tid * 4, 0, 0);
+  // columns of the workgroup per thread: one for 4 x 4 (8 groups), up to three for the others
+  constexpr int kCpt = (WgShape<kT>::kMaxGS * kGroupCols + kThreads - 1) / kThreads;
+  uint32_t src[kCpt];
+#pragma unroll
+  for (int k = 0; k < kCpt; ++k)
+    src[k] = __builtin_amdgcn_raw_buffer_load_b32(pi_rs, (tid + k * kThreads) * 4, 0, 0);
   __builtin_amdgcn_sched_barrier(0);  // keep the issue order: the counters wait in order
   const uint32_t last = (uint32_t)J.d_in - 1u;  // an out-of-range pi entry is clamped
   // identity when pi is absent, as a lane mask rather than a branch
@@ -274,7 +286,7 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int i
   UnitRegs U[kMaxUnits];
   constexpr int kChunks = kWholeXMax / 8 / kThreads;  // 16-byte chunks of x per thread
   u32x4 xc[kChunks];
-  uint16_t xv = 0;
+  uint16_t xv[kCpt] = {};
   if constexpr (kWholeX) {
     // the whole activation vector goes to LDS, so the gather x[pi[p]] becomes an LDS read
 #pragma unroll
@@ -282,8 +294,12 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int i
       xc[i] = __builtin_amdgcn_raw_buffer_load_b128(x_rs, (tid + i * kThreads) * 16, 0, 0);
   } else {
     // wide inputs: the gathered activations straight from memory, after pi
-    const uint32_t col = (min(src, last) & use_pi) | ((uint32_t)(c0 + tid) & ~use_pi);
-    xv = __builtin_amdgcn_raw_buffer_load_b16(x_rs, col * 2u, 0, 0);
+#pragma unroll
+    for (int k = 0; k < kCpt; ++k) {
+      const uint32_t c = (uint32_t)(c0 + tid + k * kThreads);
+      const uint32_t col = (min(src[k], last) & use_pi) | (c & ~use_pi);
+      xv[k] = __builtin_amdgcn_raw_buffer_load_b16(x_rs, col * 2u, 0, 0);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -303,7 +319,7 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int i
       *reinterpret_cast<u32x4*>(smem + C::kCbOff + tid * 256 + r * 16) = cw;
   }
   if constexpr (kWholeX) {
-    uint16_t* xw = reinterpret_cast<uint16_t*>(smem + tail + kTailX);
+    uint16_t* xw = reinterpret_cast<uint16_t*>(smem + tail + tail_x(kT));
     if (kFused && consumer) {
       mlp_input(J, xw, tid);
     } else {
@@ -313,10 +329,16 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int i
           *reinterpret_cast<u32x4*>(xw + (tid + i * kThreads) * 8) = xc[i];
     }
     __syncthreads();
-    const uint32_t col = (min(src, last) & use_pi) | ((uint32_t)(c0 + tid) & ~use_pi);
-    if (tid < cols) xp[tid] = xw[col];
+#pragma unroll
+    for (int k = 0; k < kCpt; ++k) {
+      const int c = tid + k * kThreads;
+      const uint32_t col = (min(src[k], last) & use_pi) | ((uint32_t)(c0 + c) & ~use_pi);
+      if (c < cols) xp[c] = xw[col];
+    }
   } else {
-    if (tid < cols) xp[tid] = xv;
+#pragma unroll
+    for (int k = 0; k < kCpt; ++k)
+      if (tid + k * kThreads < cols) xp[tid + k * kThreads] = xv[k];
   }
   __syncthreads();
   for (int e = tid; e < ngl * kSubPerGroup * 16; e += kThreads) {
@@ -394,7 +416,7 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int i
   if (kFused && J.out32 != nullptr) signal_row_group(J, tid);
 }
 
-template <bool kWholeX, bool kFused>
+template <int kT, bool kWholeX, bool kFused>
 __global__ void __launch_bounds__(kThreads) gemv_kernel(JobTable T) {
   extern __shared__ __align__(16) uint8_t smem[];
   const Job& J = T.jobs[blockIdx.y];
@@ -419,11 +441,11 @@ __global__ void __launch_bounds__(kThreads) gemv_kernel(JobTable T) {
     R.L = J.log2K;
   }
   switch (R.L) {
-    case 4: gemv_body<4, kWholeX, kFused>(R, J, inst, rq, split, smem); break;
-    case 5: gemv_body<5, kWholeX, kFused>(R, J, inst, rq, split, smem); break;
-    case 6: gemv_body<6, kWholeX, kFused>(R, J, inst, rq, split, smem); break;
-    case 7: gemv_body<7, kWholeX, kFused>(R, J, inst, rq, split, smem); break;
-    default: gemv_body<8, kWholeX, kFused>(R, J, inst, rq, split, smem); break;
+    case 4: gemv_body<4, kT, kWholeX, kFused>(R, J, inst, rq, split, smem); break;
+    case 5: gemv_body<5, kT, kWholeX, kFused>(R, J, inst, rq, split, smem); break;
+    case 6: gemv_body<6, kT, kWholeX, kFused>(R, J, inst, rq, split, smem); break;
+    case 7: gemv_body<7, kT, kWholeX, kFused>(R, J, inst, rq, split, smem); break;
+    default: gemv_body<8, kT, kWholeX, kFused>(R, J, inst, rq, split, smem); break;
   }
 }
 
@@ -436,6 +458,7 @@ struct Product {
 };
 
 struct Plan {
+  int tiles;              // workgroup shape: row tiles per workgroup (4, 2 or 1)
   int gs;                 // groups per split (before balancing per product)
   int n;                  // pieces
   Job pieces[kMaxJobs];   // planning fields filled: d_out, d_in, tile0, rt, rq, ng, S, gs, inst
@@ -443,30 +466,80 @@ struct Plan {
   int grid_x;
 };
 
-int64_t launch_wgs(const Product* p, int n, int gs) {
+int64_t launch_wgs(const Product* p, int n, int gs, int T) {
   int64_t wgs = 0;
   for (int i = 0; i < n; ++i) {
     const int ng = p[i].d_in / kGroupCols;
     const int g = gs < ng ? gs : ng;
-    wgs += (int64_t)p[i].inst * ceil_div(ceil_div(p[i].d_out, kTileRows), kTiles) * ceil_div(ng, g);
+    wgs += (int64_t)p[i].inst * ceil_div(ceil_div(p[i].d_out, kTileRows), T) * ceil_div(ng, g);
   }
   return wgs;
+}
+
+size_t lds_bytes(int maxL, int gs, int whole_d_in, int T) {
+  size_t need = 0;
+  for (int L = 4; L <= maxL; ++L) {
+    const size_t b = lds_tail(L, gs) + tail_x(T);
+    if (b > need) need = b;
+  }
+  return need + (size_t)whole_d_in * 2;
 }
 
 // Groups per split: the fewest that keep the launch within one workgroup per compute unit (a
 // workgroup fills a compute unit), so every launch runs in a single round with the least work
 // per workgroup; the largest allowed when even that does not fit.
-int plan_gs(const Product* p, int n) {
+int plan_gs(const Product* p, int n, int T) {
   const int64_t cus = device_cu_count();
-  for (int gs = 1; gs <= kMaxGroupsPerSplit; ++gs)
-    if (launch_wgs(p, n, gs) <= cus) return gs;
-  return kMaxGroupsPerSplit;
+  for (int gs = 1; gs <= shape_max_gs(T); ++gs)
+    if (launch_wgs(p, n, gs, T) <= cus) return gs;
+  return shape_max_gs(T);
 }
 
-// Cuts the products into pieces of whole row quads with similar workgroup counts, so the 2-D grid
-// (pieces x workgroups of the widest piece) wastes few workgroups.
-void plan_pieces(const Product* p, int n, Plan& P) {
-  P.gs = plan_gs(p, n);
+// Workgroup shape and groups per split of a batch-one launch. With every codebook below 256
+// entries (the tables of K = 256 leave room for 8 groups only), measured on the decoder layer:
+//   1. one split per product when a shape with more parts per tile fits it in one workgroup per
+//      compute unit: 1 x 16 first (q|k|v: 7.56 us against 7.57 us), then 2 x 8 (gate|up: 10.1 us
+//      against 10.5 us);
+//   2. else 1 x 16 with the fewest groups per split that keep one round (o: 7.6 us against 8.4 us,
+//      down: 9.3 us against 10.0 us: a tile's 16 parts leave 6 splits instead of 16 and 19);
+//   3. else the general 4 x 4 shape.
+// The LDS check assumes the input is staged whole, so the plan does not depend on the pointers.
+void plan_shape(const Product* p, int n, int maxL, bool shapes, Plan& P) {
+  P.tiles = 4;
+  P.gs = plan_gs(p, n, 4);
+  if (!shapes || maxL > 7) return;
+  const int64_t cus = device_cu_count();
+  int max_ng = 0, max_din = 0;
+  for (int i = 0; i < n; ++i) {
+    max_ng = std::max(max_ng, p[i].d_in / kGroupCols);
+    max_din = std::max(max_din, p[i].d_in);
+  }
+  const int whole = max_din <= kWholeXMax ? max_din : 0;
+  auto fits = [&](int gs, int T) {
+    return gs <= shape_max_gs(T) && launch_wgs(p, n, gs, T) <= cus &&
+           lds_bytes(maxL, gs, whole, T) <= 160 * 1024;
+  };
+  for (int T : {1, 2}) {
+    if (fits(max_ng, T)) {
+      P.tiles = T;
+      P.gs = max_ng;
+      return;
+    }
+  }
+  for (int gs = 1; gs <= shape_max_gs(1); ++gs) {
+    if (fits(gs, 1)) {
+      P.tiles = 1;
+      P.gs = gs;
+      return;
+    }
+  }
+}
+
+// Cuts the products into pieces of whole tile blocks (P.tiles row tiles) with similar workgroup
+// counts, so the 2-D grid (pieces x workgroups of the widest piece) wastes few workgroups.
+void plan_pieces(const Product* p, int n, int maxL, bool shapes, Plan& P) {
+  plan_shape(p, n, maxL, shapes, P);
+  const int kTiles = P.tiles;
   int S[kMaxJobs], gs[kMaxJobs], rq[kMaxJobs];
   int64_t count[kMaxJobs];
   int64_t smallest = INT64_MAX;
@@ -531,15 +604,6 @@ size_t plan_workspace(const Plan& P) {
   return need;
 }
 
-size_t lds_bytes(int maxL, int gs, int whole_d_in) {
-  size_t need = 0;
-  for (int L = 4; L <= maxL; ++L) {
-    const size_t b = lds_tail(L, gs) + kTailX;
-    if (b > need) need = b;
-  }
-  return need + (size_t)whole_d_in * 2;
-}
-
 // Fills the piece fields the plan leaves open (matrix, vectors, workspace) and launches.
 int launch(Plan& P, const Job* proto, bool whole, int maxL, void* ws, size_t ws_bytes,
            hipStream_t stream) {
@@ -598,25 +662,37 @@ int launch(Plan& P, const Job* proto, bool whole, int maxL, void* ws, size_t ws_
   }
   const bool fused = signals > 0;
   if (fused && !whole) return SAGE_ERR_ARG;  // the fused block stages its input whole
+  if (fused && P.tiles != 4) return SAGE_ERR_ARG;  // the fused block is built for the 4 x 4 shape
   static bool attr_done = false;
   if (!attr_done) {
-    const void* kernels[3] = {reinterpret_cast<const void*>(gemv_kernel<true, false>),
-                              reinterpret_cast<const void*>(gemv_kernel<false, false>),
-                              reinterpret_cast<const void*>(gemv_kernel<true, true>)};
+    const void* kernels[7] = {reinterpret_cast<const void*>(gemv_kernel<4, true, false>),
+                              reinterpret_cast<const void*>(gemv_kernel<4, false, false>),
+                              reinterpret_cast<const void*>(gemv_kernel<4, true, true>),
+                              reinterpret_cast<const void*>(gemv_kernel<2, true, false>),
+                              reinterpret_cast<const void*>(gemv_kernel<2, false, false>),
+                              reinterpret_cast<const void*>(gemv_kernel<1, true, false>),
+                              reinterpret_cast<const void*>(gemv_kernel<1, false, false>)};
     for (const void* k : kernels)
       if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) !=
           hipSuccess)
         return SAGE_ERR_HIP;
     attr_done = true;
   }
-  const size_t lds = lds_bytes(maxL, gs_max, whole ? d_in_max : 0);
+  const size_t lds = lds_bytes(maxL, gs_max, whole ? d_in_max : 0, P.tiles);
   const dim3 grid((unsigned)P.grid_x, (unsigned)P.n);
-  if (fused)
-    hipLaunchKernelGGL((gemv_kernel<true, true>), grid, dim3(kThreads), lds, stream, T);
-  else if (whole)
-    hipLaunchKernelGGL((gemv_kernel<true, false>), grid, dim3(kThreads), lds, stream, T);
-  else
-    hipLaunchKernelGGL((gemv_kernel<false, false>), grid, dim3(kThreads), lds, stream, T);
+  const dim3 block(kThreads);
+  if (fused) {
+    hipLaunchKernelGGL((gemv_kernel<4, true, true>), grid, block, lds, stream, T);
+  } else if (P.tiles == 1) {
+    if (whole) hipLaunchKernelGGL((gemv_kernel<1, true, false>), grid, block, lds, stream, T);
+    else hipLaunchKernelGGL((gemv_kernel<1, false, false>), grid, block, lds, stream, T);
+  } else if (P.tiles == 2) {
+    if (whole) hipLaunchKernelGGL((gemv_kernel<2, true, false>), grid, block, lds, stream, T);
+    else hipLaunchKernelGGL((gemv_kernel<2, false, false>), grid, block, lds, stream, T);
+  } else {
+    if (whole) hipLaunchKernelGGL((gemv_kernel<4, true, false>), grid, block, lds, stream, T);
+    else hipLaunchKernelGGL((gemv_kernel<4, false, false>), grid, block, lds, stream, T);
+  }
   return hip_status();
 }
 
@@ -632,17 +708,23 @@ using namespace sage;
 
 namespace {
 
-int multi_plan(const sage_matrix_t* mats, int n, Plan& P) {
+// shapes: whether the batch-one launch may use the 2 x 8 and 1 x 16 workgroup shapes (the
+// fused SwiGLU launch keeps 4 x 4)
+int multi_plan(const sage_matrix_t* mats, int n, bool shapes, Plan& P) {
   Product p[kMaxJobs];
-  for (int i = 0; i < n; ++i) p[i] = Product{mats[i].d_out, mats[i].d_in, 1};
-  plan_pieces(p, n, P);
+  int maxL = 4;
+  for (int i = 0; i < n; ++i) {
+    p[i] = Product{mats[i].d_out, mats[i].d_in, 1};
+    maxL = std::max(maxL, mats[i].log2K);
+  }
+  plan_pieces(p, n, maxL, shapes, P);
   return SAGE_OK;
 }
 
 int moe_plan(const sage_matrix_t* shapes, int n_mats, int n_sel, Plan& P) {
   Product p[kMaxJobs];
   for (int j = 0; j < n_mats; ++j) p[j] = Product{shapes[j].d_out, shapes[j].d_in, n_sel};
-  plan_pieces(p, n_mats, P);
+  plan_pieces(p, n_mats, 8, false, P);
   return SAGE_OK;
 }
 
@@ -669,7 +751,7 @@ int sage_gemv_multi_workspace_bytes(const sage_matrix_t* mats, int n, size_t* by
     if (st != SAGE_OK) return st;
   }
   Plan P;
-  multi_plan(mats, n, P);
+  multi_plan(mats, n, true, P);
   *bytes = plan_workspace(P);
   return SAGE_OK;
 }
@@ -685,7 +767,7 @@ int sage_gemv_multi(const sage_matrix_t* mats, const uint16_t* const* xs, uint16
     if (!aligned(xs[i], 4) || !aligned(ys[i], 2)) return SAGE_ERR_ALIGN;
   }
   Plan P;
-  multi_plan(mats, n, P);
+  multi_plan(mats, n, true, P);
   Job proto[kMaxJobs];
   int maxL = 4;
   bool whole = true;
@@ -728,7 +810,7 @@ int sage_mlp_workspace_bytes(const sage_matrix_t* gate, const sage_matrix_t* up,
   if (st != SAGE_OK) return st;
   const sage_matrix_t mats[3] = {*gate, *up, *down};
   Plan P;
-  multi_plan(mats, 3, P);
+  multi_plan(mats, 3, false, P);
   *bytes = plan_workspace(P) + mlp_extra_bytes(gate->d_out);
   return SAGE_OK;
 }
@@ -743,7 +825,7 @@ int sage_mlp(const sage_matrix_t* gate, const sage_matrix_t* up, const sage_matr
     return SAGE_ERR_ALIGN;
   const sage_matrix_t mats[3] = {*gate, *up, *down};
   Plan P;
-  multi_plan(mats, 3, P);
+  multi_plan(mats, 3, false, P);
   const size_t parts_bytes = plan_workspace(P);
   if (ws_bytes < parts_bytes + mlp_extra_bytes(gate->d_out)) return SAGE_ERR_WORKSPACE;
   char* extra = static_cast<char*>(ws) + parts_bytes;

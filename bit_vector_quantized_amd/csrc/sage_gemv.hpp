@@ -5,14 +5,20 @@
 
 namespace sage {
 
-// Workgroup shape: kTiles row tiles x kParts column parts, one wavefront each. The kParts waves of
-// a row tile split the workgroup's columns and add their partial sums in LDS.
-constexpr int kTiles = 4;
-constexpr int kParts = 4;
-constexpr int kWaves = kTiles * kParts;
+// Workgroup shapes: T row tiles x (16 / T) column parts, one wavefront each (16 waves, 1024
+// threads). The parts of a row tile split the workgroup's columns and add their partial sums in
+// LDS. T = 4 is the general shape; T = 2 and T = 1 put more parts on a tile, so fewer workgroups
+// of other compute units have to combine split-K partials (planner in sage_gemv.hip).
+constexpr int kWaves = 16;
 constexpr int kThreads = kWaves * 64;
-constexpr int kMaxGroupsPerSplit = 8;                         // column groups per workgroup
-constexpr int kMaxUnits = 2 * kMaxGroupsPerSplit / kParts;    // half-groups per wavefront
+template <int T>
+struct WgShape {
+  static constexpr int kTiles = T;
+  static constexpr int kParts = kWaves / T;
+  static constexpr int kMaxGS = T == 4 ? 8 : (T == 2 ? 20 : 24);           // groups per workgroup
+  static constexpr int kMaxUnits = (2 * kMaxGS + kParts - 1) / kParts;     // half-groups per wave
+};
+__host__ __device__ constexpr int shape_max_gs(int T) { return T == 4 ? 8 : (T == 2 ? 20 : 24); }
 constexpr int kMaxJobs = 16;
 constexpr int kWholeXMax = 16384;  // inputs up to this width are staged whole in LDS
 
@@ -35,7 +41,7 @@ struct Job {
   int32_t tstride, toff, n_experts;
   int32_t log2K;
   int32_t d_out, d_in;      // the whole matrix
-  int32_t tile0, rt, rq;    // first row tile, row tiles, row quads (ceil(rt / kTiles)) of the piece
+  int32_t tile0, rt, rq;    // first row tile, row tiles, tile blocks (ceil(rt / T)) of the piece
   int32_t ng;               // column groups of the matrix
   int32_t S, gs;            // column splits and groups per split
   int32_t wg_per_inst, inst;
