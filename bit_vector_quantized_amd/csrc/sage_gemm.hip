@@ -22,12 +22,19 @@
 namespace sage {
 namespace {
 
-constexpr int kGTiles = 2;                           // 64-row weight tiles per workgroup
-constexpr int kGParts = 2;                           // column parts
-constexpr int kGWaves = kGTiles * 4 * kGParts;       // 16
+// Small-batch workgroup shapes: T 64-row weight tiles (four 16-row quarter waves each) x 4/T
+// column parts, 16 waves. T = 2 is the general shape; T = 1 gives each tile 4 parts, so a row
+// tile can take all its column groups without split-K.
+constexpr int kGWaves = 16;
 constexpr int kGThreads = kGWaves * 64;              // 1024
-constexpr int kGMaxGS = 8;                           // column groups per split
-constexpr int kGMaxUnits = kGMaxGS / kGParts;        // groups per wavefront
+template <int T>
+struct GShape {
+  static constexpr int kTiles = T;
+  static constexpr int kParts = 4 / T;
+  static constexpr int kMaxGS = T == 2 ? 8 : 20;                            // groups per split
+  static constexpr int kMaxUnits = (kMaxGS + kParts - 1) / kParts;          // groups per wave
+};
+inline int gshape_max_gs(int T) { return T == 2 ? 8 : 20; }
 constexpr int kPermuteMinRows = 8;                   // from this many rows on, X is permuted once
 constexpr int kDirectRows = kPermuteMinRows;         // rows gathered straight from X below that
 constexpr int kPrefillMinRows = 128;                 // prefill kernel candidates from this many rows
@@ -46,12 +53,13 @@ struct GemmArgs {
   const uint16_t* X;
   uint16_t* Y;
   float* partial;       // [mchunk][split][mrows_chunk][rt * 64]
-  uint32_t* counters;   // [mchunk][rpairs]
+  uint32_t* counters;   // [mchunk][rpairs] (rpairs = tile blocks of the shape)
   int64_t ldx, ldy;
   int32_t d_out, d_in, M, L;
   int32_t rt, rpairs, ng, S, gs, mchunks;
   int32_t mrows_chunk;  // activation rows per workgroup = 16 * NT
   int32_t vec_x;        // X rows are 16-byte aligned and already in permuted order (kVec)
+  int32_t tiles;        // workgroup shape (GShape<tiles>)
 };
 
 __device__ inline __amdgpu_buffer_rsrc_t view(const void* base, uint32_t bytes) {
@@ -199,9 +207,12 @@ __device__ inline uint32_t mul_pair(uint32_t c, half2_t r) {
 // [NT*16][gs*128 + 8] fp16 (also the part-sum exchange once the products are done).
 __host__ __device__ inline uint32_t gemm_xs_offset(int L) { return (1u << L) * 256u + 144u; }
 
-template <int L, int NT, bool kVec>
+template <int L, int NT, bool kVec, int kGT>
 __device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint8_t* smem) {
   constexpr uint32_t kK = 1u << L;
+  constexpr int kGTiles = GShape<kGT>::kTiles;
+  constexpr int kGParts = GShape<kGT>::kParts;
+  constexpr int kGMaxUnits = GShape<kGT>::kMaxUnits;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -233,15 +244,19 @@ __device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint
   const u32x4 cw = __builtin_amdgcn_raw_buffer_load_b128(cb_rs, tid * 16, 0, 0);
   const __amdgpu_buffer_rsrc_t x_rs =
       view(A.X + (int64_t)m0 * A.ldx, (uint32_t)((int64_t)mrows * A.ldx * 2));
-  constexpr int kVecLoads = 2 * NT;  // 16-byte chunks per thread: NT*16 rows x 128 chunks
+  // 16-byte chunks per staged row (the shape's largest split) and per thread
+  constexpr int kCpr = GShape<kGT>::kMaxGS * (kGroupCols / 8);
+  constexpr int kVecLoads = (NT * 16 * kCpr + kGThreads - 1) / kGThreads;
+  // columns per thread on the gathered path (more than one when a split exceeds 1024 columns)
+  constexpr int kCpt = (GShape<kGT>::kMaxGS * kGroupCols + kGThreads - 1) / kGThreads;
   u32x4 xc[kVecLoads];
-  uint16_t xv[kDirectRows];
+  uint16_t xv[kCpt][kDirectRows];
   const int nck = ngl * (kGroupCols / 8);
   if constexpr (kVec) {
 #pragma unroll
     for (int i = 0; i < kVecLoads; ++i) {
       const int e = tid + i * kGThreads;
-      const int m = e >> 7, ch = e & 127;
+      const int m = e / kCpr, ch = e % kCpr;
       const uint32_t off =
           ch < nck ? (uint32_t)(((int64_t)m * A.ldx + c0 + ch * 8) * 2) : kNowhere;
       xc[i] = __builtin_amdgcn_raw_buffer_load_b128(x_rs, off, 0, 0);
@@ -265,12 +280,16 @@ __device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint
     // few rows in original order: gather through pi straight from X (rows >= mrows read zeros)
     const __amdgpu_buffer_rsrc_t pi_rs =
         view(A.pi ? A.pi + c0 : nullptr, A.pi ? (uint32_t)cols * 4u : 0u);
-    const uint32_t pv = __builtin_amdgcn_raw_buffer_load_b32(pi_rs, tid * 4, 0, 0);
-    const uint32_t src = A.pi ? min(pv, (uint32_t)A.d_in - 1u) : (uint32_t)(c0 + tid);
 #pragma unroll
-    for (int m = 0; m < kDirectRows; ++m)
-      xv[m] = __builtin_amdgcn_raw_buffer_load_b16(
-          x_rs, tid < cols ? (uint32_t)(((int64_t)m * A.ldx + src) * 2) : kNowhere, 0, 0);
+    for (int q = 0; q < kCpt; ++q) {
+      const int c = tid + q * kGThreads;
+      const uint32_t pv = __builtin_amdgcn_raw_buffer_load_b32(pi_rs, c * 4, 0, 0);
+      const uint32_t src = A.pi ? min(pv, (uint32_t)A.d_in - 1u) : (uint32_t)(c0 + c);
+#pragma unroll
+      for (int m = 0; m < kDirectRows; ++m)
+        xv[q][m] = __builtin_amdgcn_raw_buffer_load_b16(
+            x_rs, c < cols ? (uint32_t)(((int64_t)m * A.ldx + src) * 2) : kNowhere, 0, 0);
+    }
   }
 
   // 2. LDS set-up.
@@ -282,13 +301,20 @@ __device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint
 #pragma unroll
     for (int i = 0; i < kVecLoads; ++i) {
       const int e = tid + i * kGThreads;
-      const int m = e >> 7, ch = e & 127;
-      if (ch < nck) *reinterpret_cast<u32x4*>(xs + m * xstride + ch * 8) = xc[i];
+      const int m = e / kCpr, ch = e % kCpr;
+      if (ch < nck && m < NT * 16) *reinterpret_cast<u32x4*>(xs + m * xstride + ch * 8) = xc[i];
     }
-  } else if (tid < cols) {
+  } else {
 #pragma unroll
-    for (int m = 0; m < 16; ++m)
-      xs[m * xstride + tid] = m < kDirectRows ? __builtin_bit_cast(_Float16, xv[m]) : (_Float16)0.0f;
+    for (int q = 0; q < kCpt; ++q) {
+      const int c = tid + q * kGThreads;
+      if (c < cols) {
+#pragma unroll
+        for (int m = 0; m < 16; ++m)
+          xs[m * xstride + c] =
+              m < kDirectRows ? __builtin_bit_cast(_Float16, xv[q][m]) : (_Float16)0.0f;
+      }
+    }
   }
   __syncthreads();
 
@@ -341,17 +367,22 @@ __device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint
     }
   }
 
-  // 4. The second column part hands its sums to the first through LDS (the X tile is done).
+  // 4. The other column parts hand their sums to the first through LDS (the X tile is done);
+  // part order is kept.
   __syncthreads();
   float4_t* red = reinterpret_cast<float4_t*>(xs);
-  if (part == 1) {
+  if (part > 0) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) red[(quarter * NT + t) * 64 + lane] = acc[t];
+    for (int t = 0; t < NT; ++t)
+      red[(((part - 1) * kGTiles * 4 + quarter) * NT + t) * 64 + lane] = acc[t];
   }
   __syncthreads();
   if (part == 0) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] += red[(quarter * NT + t) * 64 + lane];
+    for (int p = 1; p < kGParts; ++p)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        acc[t] += red[(((p - 1) * kGTiles * 4 + quarter) * NT + t) * 64 + lane];
   }
 
   // 5. Output. D layout: lane holds weight row j and activation rows 4u .. 4u+3 of each tile.
@@ -386,12 +417,14 @@ __device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint
   if (tid == 0) *flag = (counter_add(counter) == (uint32_t)(A.S - 1)) ? 1u : 0u;
   __syncthreads();
   if (*flag == 0u) return;
-  // last workgroup: reduce both tiles for all rows of the chunk. Thread t owns elements
-  // t + 1024 i (activation row e / 128, row e % 128 of the tile pair); four splits in flight.
-  constexpr int kPer = NT * 16 * kGTiles * kTileRows / kGThreads;
+  // last workgroup: reduce the tiles for all rows of the chunk. Thread t owns elements
+  // t + 1024 i (activation row e / R, row e % R of the tile block, R = 64 kGTiles); four splits in
+  // flight.
+  constexpr int kRows = kGTiles * kTileRows;
+  constexpr int kPer = NT * 16 * kRows / kGThreads;
   const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(
       pbuf, (uint32_t)((int64_t)A.S * A.mrows_chunk * rows_pad * (int64_t)sizeof(float)));
-  const int prow = rp * kGTiles * kTileRows + (tid & 127);
+  const int prow = rp * kRows + (tid % kRows);
   float sum[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) sum[i] = 0.0f;
@@ -401,7 +434,7 @@ __device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
-        const int m = (tid >> 7) + 8 * i;
+        const int m = tid / kRows + (kGThreads / kRows) * i;
         const int sp = min(sp0 + q, A.S - 1);
         v[q][i] = load_coherent_at(
             rs, (uint32_t)((((int64_t)sp * A.mrows_chunk + m) * rows_pad + prow) * sizeof(float)));
@@ -415,14 +448,14 @@ __device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint
   if (prow < A.d_out) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int m = (tid >> 7) + 8 * i;
+      const int m = tid / kRows + (kGThreads / kRows) * i;
       if (m < mrows) A.Y[(int64_t)(m0 + m) * A.ldy + prow] = f2h(sum[i]);
     }
   }
   if (tid == 0) counter_reset(counter);
 }
 
-template <int NT, bool kVec>
+template <int NT, bool kVec, int kGT>
 __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs A) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int per_chunk = A.rpairs * A.S;
@@ -431,13 +464,15 @@ __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs A) {
   const int rp = local / A.S;
   const int split = local - rp * A.S;
   switch (A.L) {
-    case 4: gemm_body<4, NT, kVec>(A, rp, split, mchunk, smem); break;
-    case 5: gemm_body<5, NT, kVec>(A, rp, split, mchunk, smem); break;
-    case 6: gemm_body<6, NT, kVec>(A, rp, split, mchunk, smem); break;
-    case 7: gemm_body<7, NT, kVec>(A, rp, split, mchunk, smem); break;
-    default: gemm_body<8, NT, kVec>(A, rp, split, mchunk, smem); break;
+    case 4: gemm_body<4, NT, kVec, kGT>(A, rp, split, mchunk, smem); break;
+    case 5: gemm_body<5, NT, kVec, kGT>(A, rp, split, mchunk, smem); break;
+    case 6: gemm_body<6, NT, kVec, kGT>(A, rp, split, mchunk, smem); break;
+    case 7: gemm_body<7, NT, kVec, kGT>(A, rp, split, mchunk, smem); break;
+    default: gemm_body<8, NT, kVec, kGT>(A, rp, split, mchunk, smem); break;
   }
 }
+
+typedef void (*GemmFn)(GemmArgs);
 
 // ------------------------------------------------------------------------------------------------
 // Prefill-sized batches (SAGE paper §3.5 / Fig. 6b: decode each weight once per output tile and
@@ -884,25 +919,41 @@ int tiles_for(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
 
 constexpr size_t kLdsLimit = 160 * 1024;
 
-size_t lds_for(int L, int nt, int gs) {
+// LDS of the small-batch kernel: codebook, then the X tile or the part-sum exchange (T tiles,
+// 4 / T parts), whichever is larger.
+size_t lds_for(int L, int nt, int gs, int T) {
   const size_t xtile = (size_t)nt * 16 * ((size_t)gs * kGroupCols + 8) * 2;
-  const size_t red = (size_t)kGTiles * 4 * nt * 64 * 16;
+  const size_t red = (size_t)(4 / T - 1) * T * 4 * nt * 64 * 16;
   return gemm_xs_offset(L) + (xtile > red ? xtile : red);
 }
 
-// Groups per split: the fewest that keep the launch within one workgroup per compute unit (a
-// workgroup fills a compute unit) and the LDS budget.
+// Workgroup shape and groups per split (a workgroup fills a compute unit, so a launch should fit
+// in one workgroup per compute unit):
+//   1. 8 to 16 activation rows (read as whole vectors, not gathered): 1 x 4 with every column
+//      group in one split when that fits (no split-K at all; more rows would not fit the LDS with
+//      twenty groups, and with fewer the per-thread gather of twenty groups costs more than the
+//      split-K pass it saves);
+//   2. else 2 x 2 with the fewest groups per split that fit, within the LDS budget.
 void plan(GemmArgs& A, int M) {
   A.rt = ceil_div(A.d_out, kTileRows);
-  A.rpairs = ceil_div(A.rt, kGTiles);
   A.ng = A.d_in / kGroupCols;
   A.mrows_chunk = 16 * tiles_for(M);
   A.mchunks = ceil_div(M, A.mrows_chunk);
   const int nt = tiles_for(M);
   const int64_t cus = device_cu_count();
+  if (nt == 1 && M >= kPermuteMinRows && A.ng <= gshape_max_gs(1) && (int64_t)A.mchunks * A.rt <= cus &&
+      lds_for(A.L, nt, A.ng, 1) <= kLdsLimit) {
+    A.tiles = 1;
+    A.rpairs = A.rt;
+    A.S = 1;
+    A.gs = A.ng;
+    return;
+  }
+  A.tiles = 2;
+  A.rpairs = ceil_div(A.rt, 2);
   int best = 1;
-  for (int gs = 1; gs <= kGMaxGS && gs <= A.ng; ++gs) {
-    if (lds_for(A.L, nt, gs) > kLdsLimit) break;
+  for (int gs = 1; gs <= gshape_max_gs(2) && gs <= A.ng; ++gs) {
+    if (lds_for(A.L, nt, gs, 2) > kLdsLimit) break;
     best = gs;
     if ((int64_t)A.mchunks * A.rpairs * ceil_div(A.ng, gs) <= cus) break;
   }
@@ -1056,21 +1107,26 @@ int sage_gemm_small(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, u
     A.vec_x = 0;  // fewer than kPermuteMinRows rows, gathered through pi by the kernel
   }
   const int nt = tiles_for(M);
-  const size_t lds = lds_for(A.L, nt, A.gs);
+  const size_t lds = lds_for(A.L, nt, A.gs, A.tiles);
   const unsigned grid = (unsigned)(A.mchunks * A.rpairs * A.S);
-  auto launch = [&](auto kern) {
-    static bool attr = false;
-    if (!attr) {
+  // Each instantiation gets its LDS limit raised once (slot = shape * 4 + variant).
+  static bool attr_set[8] = {};
+  auto launch = [&](GemmFn kern, int slot) {
+    if (!attr_set[slot]) {
       (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-      attr = true;
+      attr_set[slot] = true;
     }
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kGThreads), lds, hs, A);
   };
-  if (!A.vec_x) launch(gemm_kernel<1, false>);  // fewer than kPermuteMinRows rows: nt == 1
-  else if (nt == 1) launch(gemm_kernel<1, true>);
-  else if (nt == 2) launch(gemm_kernel<2, true>);
-  else launch(gemm_kernel<4, true>);
+  if (A.tiles == 1) {  // nt == 1, whole-vector rows
+    launch(gemm_kernel<1, true, 1>, 1);
+  } else {
+    if (!A.vec_x) launch(gemm_kernel<1, false, 2>, 4);  // fewer than kPermuteMinRows rows: nt == 1
+    else if (nt == 1) launch(gemm_kernel<1, true, 2>, 5);
+    else if (nt == 2) launch(gemm_kernel<2, true, 2>, 6);
+    else launch(gemm_kernel<4, true, 2>, 7);
+  }
   return hip_status();
 }
 

@@ -389,6 +389,21 @@ def test_gemm_small_shapes(M, K, V):
     check_gemm(f"130x1152 K={K} M={M}", c, X, Y)
 
 
+@pytest.mark.parametrize("d_in", [2560, 2688])
+@pytest.mark.parametrize("M", [3, 12, 16])
+def test_gemm_small_workgroup_shapes(M, d_in):
+    """Up to sixteen rows with at most twenty column groups run as one split of 1 x 4 workgroups
+    (d_in 2560); twenty-one groups fall back to 2 x 2 with split-K (d_in 2688). A ragged last
+    row tile (70 rows) in both."""
+    import torch
+    rng = W.rng_for(143, M, d_in)
+    c = W.draw_codes(rng, 70, d_in, 64, 4)
+    X = W.draw_x(rng, (M, d_in))
+    p = upload_pack(c)
+    Y = sage.gemm_small(p, torch.from_numpy(X).cuda())
+    check_gemm(f"70x{d_in} M={M}", c, X, Y)
+
+
 @pytest.mark.parametrize("M", [1, 4, 16, 64])
 @pytest.mark.parametrize("shape", [(9728, 2560), (2560, 9728)])
 def test_gemm_small_full_size(shape, M):
