@@ -251,10 +251,13 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int i
   const int ngl = min(J.ng - g0, J.gs);
   const int rt = rq * kTiles + tile;  // row tile inside the piece
   const bool tile_ok = rt < J.rt;
+  // Half-groups of this wave (<= kMaxUnits): the first units % kParts parts take one more. The
+  // waves of one SIMD hold parts that are kParts / 4 apart, so every SIMD gets the same share.
   const int units = 2 * ngl;
-  const int upp = (units + kParts - 1) / kParts;
-  const int u0 = part * upp;
-  const int nu = max(0, min(units - u0, upp));  // half-groups of this wave (<= kMaxUnits)
+  const int ubase = units / kParts;
+  const int uextra = units - ubase * kParts;
+  const int u0 = part * ubase + min(part, uextra);
+  const int nu = ubase + (part < uextra ? 1 : 0);
   const int c0 = g0 * kGroupCols;
   const int cols = ngl * kGroupCols;
   const uint32_t tail = lds_tail(L, J.gs);
@@ -352,18 +355,26 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int i
   }
   __syncthreads();
 
-  // 3. Decode and multiply this wave's half-groups.
+  // 3. Decode and multiply this wave's half-groups. The four waves of a SIMD share its issue
+  // slots, which go to the oldest wave first; a wave's priority is its remaining work (3 down to
+  // 0), so the waves advance together and the SIMD stays busy until the last one ends.
   float acc = 0.0f;
   const uint32_t laneoff = (uint32_t)(lane & 15) * 16u;
   const uint32_t expo = C::kExpo;
+  __builtin_amdgcn_s_setprio(3);
 #pragma unroll
   for (int k = 0; k < kMaxUnits; ++k) {
     if (k < nu) {
       const uint32_t u = (uint32_t)(u0 + k);
       const uint32_t tb = C::kXtOff + (u >> 1) * (kSubPerGroup * 256) + (u & 1) * (8 * 256);
       acc = half_dot<L>(U[k], u & 1, tb, laneoff, expo, acc);
+      const int left = nu - 1 - k;
+      if (left == 2) __builtin_amdgcn_s_setprio(2);
+      else if (left == 1) __builtin_amdgcn_s_setprio(1);
+      else if (left == 0) __builtin_amdgcn_s_setprio(0);
     }
   }
+  __builtin_amdgcn_s_setprio(0);
 
   // 4. Column parts of a row tile add up in LDS (in part order).
   if (part > 0) red[((part - 1) * kTiles + tile) * 64 + lane] = acc;
