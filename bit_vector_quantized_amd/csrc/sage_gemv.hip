@@ -93,12 +93,14 @@ __host__ __device__ inline uint32_t lds_tail(int L, int gs) {
   return (L == 8) ? 98304u : (1u << L) * 256u + (uint32_t)gs * kSubPerGroup * 256u;
 }
 // Offsets inside the tail for workgroup shape T (row tiles): gathered columns fp16 [max gs * 128],
-// part sums f32 [parts - 1][T][64], flag, whole x fp16 [d_in] when staged.
+// part sums f32 [parts - 1][T][64] (chunked shape: [16 waves][64]), flag, whole x fp16 [d_in]
+// when staged.
 constexpr uint32_t kTailXp = 0;
 __host__ __device__ constexpr uint32_t tail_red(int T) { return shape_max_gs(T) * kGroupCols * 2; }
-__host__ __device__ constexpr uint32_t tail_flag(int T) {
-  return tail_red(T) + (kWaves / T - 1) * T * 64 * 4;
+__host__ __device__ constexpr uint32_t red_bytes(int T) {
+  return T == 0 ? kWaves * 64 * 4 : (kWaves / T - 1) * T * 64 * 4;
 }
+__host__ __device__ constexpr uint32_t tail_flag(int T) { return tail_red(T) + red_bytes(T); }
 __host__ __device__ constexpr uint32_t tail_x(int T) { return (tail_flag(T) + 16 + 255) / 256 * 256; }
 
 struct Resolved {
@@ -236,8 +238,8 @@ __device__ inline void mlp_input(const Job& J, uint16_t* xw, int tid) {
 }
 
 template <int L, int kT, bool kWholeX, bool kFused>
-__device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int inst, int rq,
-                                          int split, uint8_t* smem) {
+__device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, const ChunkMap& CM,
+                                          int inst, int rq, int split, uint8_t* smem) {
   using C = SplitC<L>;
   constexpr int kTiles = WgShape<kT>::kTiles;
   constexpr int kParts = WgShape<kT>::kParts;
@@ -245,6 +247,23 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int i
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: addresses in SGPRs
   const int lane = tid & 63;
+  // chunked shape: this wave's entries of the work map, read first (their latency then overlaps
+  // that of the piece's fields)
+  uint32_t cm_lo = 0, cm_hi = 0, cm_red[8] = {};
+  int wmax = 0, presum = 0;
+  if constexpr (kT == 0) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      cm_red[q] = CM.red[q];
+      asm volatile("" ::"s"(cm_red[q]));  // scalar loads, issued now
+    }
+    cm_lo = *reinterpret_cast<const uint32_t*>(&CM.lane_group[wave * 4]);
+    cm_hi = *reinterpret_cast<const uint32_t*>(&CM.lane_group[wave * 4 + 2]);
+    const uint32_t wi = CM.wave[wave];
+    wmax = (int)(wi & 255u);
+    presum = (int)(wi >> 8);
+    asm volatile("" ::"s"(cm_lo), "s"(cm_hi), "s"(wi));  // issue these loads now
+  }
   const int tile = wave % kTiles;
   const int part = wave / kTiles;
   const int g0 = split * J.gs;
@@ -258,6 +277,17 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int i
   const int uextra = units - ubase * kParts;
   const int u0 = part * ubase + min(part, uextra);
   const int nu = ubase + (part < uextra ? 1 : 0);
+  // Chunked shape: this lane group's chunk and half-group range (us, un), and the wave's steps.
+  int ck = 0, us = 0, un = 0;
+  if constexpr (kT == 0) {
+    const int lg = lane >> 4;
+    const uint32_t e = ((lg & 2) ? cm_hi : cm_lo) >> ((lg & 1) * 16);
+    ck = (int)(e & 15u);
+    un = (int)((e >> 4) & 15u);
+    us = (int)((e >> 8) & 255u);
+  }
+  const int gchunk = J.chunk0 + rq * J.cq + ck;  // chunk of the matrix (chunked shape)
+  const bool chunk_ok = kT == 0 && ck < J.cq && gchunk < J.chunk0 + J.nchunk;
   const int c0 = g0 * kGroupCols;
   const int cols = ngl * kGroupCols;
   const uint32_t tail = lds_tail(L, J.gs);
@@ -271,8 +301,12 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int i
   const bool consumer = kFused && J.src_gate != nullptr;  // input built in LDS from a first stage
   const __amdgpu_buffer_rsrc_t x_rs =
       view(consumer ? nullptr : J.x + (int64_t)inst * J.x_stride, consumer ? 0u : (uint32_t)J.d_in * 2u);
-  const uint8_t* blk0 = R.packed + ((int64_t)(J.tile0 + rt) * J.ng + g0) * kBlockBytes;
-  const __amdgpu_buffer_rsrc_t w_rs = view(blk0, tile_ok ? (uint32_t)(ngl * kBlockBytes) : 0u);
+  const uint8_t* blk0 =
+      kT == 0 ? R.packed : R.packed + ((int64_t)(J.tile0 + rt) * J.ng + g0) * kBlockBytes;
+  const uint32_t w_bytes =
+      kT == 0 ? (uint32_t)((J.d_out + kTileRows - 1) / kTileRows * J.ng * kBlockBytes)
+              : (tile_ok ? (uint32_t)(ngl * kBlockBytes) : 0u);
+  const __amdgpu_buffer_rsrc_t w_rs = view(blk0, w_bytes);
 
   const u32x4 cw = __builtin_amdgcn_raw_buffer_load_b128(cb_rs, tid * 16, 0, 0);
   // columns of the workgroup per thread: one for 4 x 4 (8 groups), up to three for the others
@@ -305,13 +339,27 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int i
     }
   }
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (kT == 0) {
+    // lane l: row 16 * gchunk + l % 16, i.e. row (gchunk % 4) * 16 + l % 16 of tile gchunk / 4
+    const uint32_t rin = (uint32_t)((gchunk & 3) * kChunkRows + (lane & 15));
+    const uint32_t tbase = (uint32_t)((gchunk >> 2) * J.ng + g0) * kBlockBytes;
 #pragma unroll
-  for (int k = 0; k < kMaxUnits; ++k) {
-    const int u = u0 + k;
-    const uint32_t blk = (uint32_t)(u >> 1) * kBlockBytes;
-    const bool ok = k < nu;
-    load_unit(U[k], w_rs, ok ? blk + ((u & 1) ? kPlaneB : kPlaneA) + lane * 16 : kNowhere,
-              ok ? blk + kSidePlane + lane * 8 : kNowhere);
+    for (int k = 0; k < kMaxUnits; ++k) {
+      const int u = us + k;
+      const uint32_t blk = tbase + (uint32_t)(u >> 1) * kBlockBytes;
+      const bool ok = chunk_ok && k < un;
+      load_unit(U[k], w_rs, ok ? blk + ((u & 1) ? kPlaneB : kPlaneA) + rin * 16 : kNowhere,
+                ok ? blk + kSidePlane + rin * 8 : kNowhere);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kMaxUnits; ++k) {
+      const int u = u0 + k;
+      const uint32_t blk = (uint32_t)(u >> 1) * kBlockBytes;
+      const bool ok = k < nu;
+      load_unit(U[k], w_rs, ok ? blk + ((u & 1) ? kPlaneB : kPlaneA) + lane * 16 : kNowhere,
+                ok ? blk + kSidePlane + lane * 8 : kNowhere);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -362,19 +410,68 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, int i
   const uint32_t laneoff = (uint32_t)(lane & 15) * 16u;
   const uint32_t expo = C::kExpo;
   __builtin_amdgcn_s_setprio(3);
+  const int nloop = kT == 0 ? wmax : nu;
 #pragma unroll
   for (int k = 0; k < kMaxUnits; ++k) {
-    if (k < nu) {
-      const uint32_t u = (uint32_t)(u0 + k);
-      const uint32_t tb = C::kXtOff + (u >> 1) * (kSubPerGroup * 256) + (u & 1) * (8 * 256);
-      acc = half_dot<L>(U[k], u & 1, tb, laneoff, expo, acc);
-      const int left = nu - 1 - k;
+    if (k < nloop) {
+      if constexpr (kT == 0) {
+        // lane groups past their range keep their sum (their unit, clamped into the split,
+        // addresses valid tables; its zero-filled payload is discarded)
+        const uint32_t u = (uint32_t)min(us + k, units - 1);
+        const uint32_t tb = C::kXtOff + (u >> 1) * (kSubPerGroup * 256) + (u & 1) * (8 * 256);
+        const float a2 = half_dot<L>(U[k], u & 1, tb, laneoff, expo, acc);
+        acc = k < un ? a2 : acc;
+      } else {
+        const uint32_t u = (uint32_t)(u0 + k);
+        const uint32_t tb = C::kXtOff + (u >> 1) * (kSubPerGroup * 256) + (u & 1) * (8 * 256);
+        acc = half_dot<L>(U[k], u & 1, tb, laneoff, expo, acc);
+      }
+      const int left = nloop - 1 - k;
       if (left == 2) __builtin_amdgcn_s_setprio(2);
       else if (left == 1) __builtin_amdgcn_s_setprio(1);
       else if (left == 0) __builtin_amdgcn_s_setprio(0);
     }
   }
   __builtin_amdgcn_s_setprio(0);
+
+  if constexpr (kT == 0) {
+    // Chunked shape (one split): the lane groups of a chunk add up in a fixed order, main waves
+    // first, then the remaining-chunk lane groups; thread t sums row t % 16 of chunk t / 16.
+    if (presum >= 2) acc += __shfl_xor(acc, 16);
+    if (presum >= 1) acc += __shfl_xor(acc, 32);
+    red[wave * 64 + lane] = acc;
+    __syncthreads();
+    if (tid < J.cq * kChunkRows) {
+      const int c = tid >> 4, r = tid & 15;
+      uint32_t rm = cm_red[0];
+#pragma unroll
+      for (int q = 1; q < 8; ++q) rm = c == q ? cm_red[q] : rm;
+      const int first = (int)(rm & 63u), step = (int)((rm >> 6) & 63u), count = (int)(rm >> 12);
+      // sixteen LDS reads in flight at a time (zero past the last contributor), added as a fixed
+      // pairwise tree
+      float sum = 0.0f;
+      for (int i0 = 0; i0 < count; i0 += 16) {
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float t = red[min(first + (i0 + i) * step, 63) * 16 + r];
+          v[i] = i0 + i < count ? t : 0.0f;
+        }
+#pragma unroll
+        for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+          for (int i = 0; i < w; ++i) v[i] = v[2 * i] + v[2 * i + 1];
+        sum += v[0];
+      }
+      const int gc = J.chunk0 + rq * J.cq + c;
+      const int row = gc * kChunkRows + r;
+      if (gc < J.chunk0 + J.nchunk && row < J.d_out) {
+        uint16_t* yv = J.y + (int64_t)inst * J.y_stride;
+        yv[row] = f2h(sum);
+      }
+    }
+    return;
+  }
 
   // 4. Column parts of a row tile add up in LDS (in part order).
   if (part > 0) red[((part - 1) * kTiles + tile) * 64 + lane] = acc;
@@ -431,6 +528,22 @@ template <int kT, bool kWholeX, bool kFused>
 __global__ void __launch_bounds__(kThreads) gemv_kernel(JobTable T) {
   extern __shared__ __align__(16) uint8_t smem[];
   const Job& J = T.jobs[blockIdx.y];
+  // Touch every 64-byte line of the piece (and of the chunk map) at once, so the argument reads
+  // that follow (several depend on one another through branches) hit the scalar cache instead of
+  // waiting for one memory round trip each.
+  {
+    const uint32_t* jw = reinterpret_cast<const uint32_t*>(&J);
+    constexpr int kLast = (int)(sizeof(Job) / 4) - 1;
+    const uint32_t a0 = jw[0], a1 = jw[16], a2 = jw[32], a3 = jw[48 < kLast ? 48 : kLast],
+                   a4 = jw[kLast];
+    asm volatile("" ::"s"(a0), "s"(a1), "s"(a2), "s"(a3), "s"(a4));
+    if constexpr (kT == 0) {
+      const uint32_t* cw = reinterpret_cast<const uint32_t*>(&T.cmap);
+      constexpr int kCLast = (int)(sizeof(ChunkMap) / 4) - 1;
+      const uint32_t c0 = cw[0], c1 = cw[16], c2 = cw[32], c3 = cw[kCLast];
+      asm volatile("" ::"s"(c0), "s"(c1), "s"(c2), "s"(c3));
+    }
+  }
   int local = blockIdx.x;
   if (local >= J.wg_per_inst * J.inst) return;  // the grid is as wide as the widest piece
   const int inst = local / J.wg_per_inst;
@@ -452,11 +565,11 @@ __global__ void __launch_bounds__(kThreads) gemv_kernel(JobTable T) {
     R.L = J.log2K;
   }
   switch (R.L) {
-    case 4: gemv_body<4, kT, kWholeX, kFused>(R, J, inst, rq, split, smem); break;
-    case 5: gemv_body<5, kT, kWholeX, kFused>(R, J, inst, rq, split, smem); break;
-    case 6: gemv_body<6, kT, kWholeX, kFused>(R, J, inst, rq, split, smem); break;
-    case 7: gemv_body<7, kT, kWholeX, kFused>(R, J, inst, rq, split, smem); break;
-    default: gemv_body<8, kT, kWholeX, kFused>(R, J, inst, rq, split, smem); break;
+    case 4: gemv_body<4, kT, kWholeX, kFused>(R, J, T.cmap, inst, rq, split, smem); break;
+    case 5: gemv_body<5, kT, kWholeX, kFused>(R, J, T.cmap, inst, rq, split, smem); break;
+    case 6: gemv_body<6, kT, kWholeX, kFused>(R, J, T.cmap, inst, rq, split, smem); break;
+    case 7: gemv_body<7, kT, kWholeX, kFused>(R, J, T.cmap, inst, rq, split, smem); break;
+    default: gemv_body<8, kT, kWholeX, kFused>(R, J, T.cmap, inst, rq, split, smem); break;
   }
 }
 
@@ -469,7 +582,8 @@ struct Product {
 };
 
 struct Plan {
-  int tiles;              // workgroup shape: row tiles per workgroup (4, 2 or 1)
+  int tiles;              // workgroup shape: row tiles per workgroup (4, 2 or 1; 0 = chunked)
+  int cq, cwm;            // chunked shape: chunks per workgroup, waves on whole quads
   int gs;                 // groups per split (before balancing per product)
   int n;                  // pieces
   Job pieces[kMaxJobs];   // planning fields filled: d_out, d_in, tile0, rt, rq, ng, S, gs, inst
@@ -506,6 +620,112 @@ int plan_gs(const Product* p, int n, int T) {
   return shape_max_gs(T);
 }
 
+// Issue-slot cost of a workgroup: the largest number of half-group steps one SIMD runs (wave w
+// sits on SIMD w % 4 and a wave steps as long as its longest lane group).
+int shape_cost(int T, int units) {
+  const int parts = kWaves / T;
+  const int base = units / parts, extra = units % parts;
+  int worst = 0;
+  for (int s = 0; s < 4; ++s) {
+    int sum = 0;
+    for (int w = s; w < kWaves; w += 4) {
+      const int part = w / T;
+      sum += base + (part < extra ? 1 : 0);
+    }
+    worst = std::max(worst, sum);
+  }
+  return worst;
+}
+
+// Work map of the chunked shape with Q chunks, cwm main waves and `units` half-groups per lane
+// (ChunkMap in sage_gemv.hpp). Main waves take the whole quads of chunks: wave w works on quad
+// w % (Q / 4), lane group g on chunk 4 (w % (Q / 4)) + g, all four on the same half-group range
+// (so they read the same table rows); the quad's ranges split the half-groups evenly. The other
+// waves take the Q % 4 remaining chunks: lane group h (counted from the first such wave) works
+// on remaining chunk h % (Q % 4) with its own range. Returns the issue-slot cost (largest sum of
+// wave steps on one SIMD, wave w on SIMD w % 4), or -1 when a lane group would get more than
+// kMaxChunkUnits half-groups.
+int chunk_map(int Q, int cwm, int units, ChunkMap& M) {
+  const int nq = Q >> 2, nb = Q & 3;
+  M = ChunkMap{};
+  for (int w = 0; w < kWaves; ++w) {
+    int longest = 0;
+    for (int g = 0; g < 4; ++g) {
+      int ck, us, un;
+      if (w < cwm) {
+        const int a = w % nq, ri = w / nq;
+        const int nr = (cwm - a + nq - 1) / nq;
+        ck = 4 * a + g;
+        us = ri * (units / nr) + std::min(ri, units % nr);
+        un = units / nr + (ri < units % nr ? 1 : 0);
+      } else {
+        const int nr = 4 * (kWaves - cwm) / nb;
+        const int h = (w - cwm) * 4 + g, ri = h / nb;
+        ck = 4 * nq + h % nb;
+        const bool valid = h < nr * nb;
+        us = valid ? ri * (units / nr) + std::min(ri, units % nr) : 0;
+        un = valid ? units / nr + (ri < units % nr ? 1 : 0) : 0;
+      }
+      if (un > kMaxChunkUnits) return -1;
+      M.lane_group[w * 4 + g] = (uint16_t)(ck | (un << 4) | (us << 8));
+      longest = std::max(longest, un);
+    }
+    const int presum = w < cwm ? 0 : (nb == 1 ? 2 : (nb == 2 ? 1 : 0));
+    M.wave[w] = (uint32_t)longest | ((uint32_t)presum << 8);
+  }
+  for (int c = 0; c < Q; ++c) {
+    int first, step, count;
+    if (c < 4 * nq) {
+      first = (c >> 2) * 4 + (c & 3);
+      step = 4 * nq;
+      count = (cwm - (c >> 2) + nq - 1) / nq;
+    } else if (nb <= 2) {  // summed inside each wave first: lane group c - 4 nq of every wave
+      first = 4 * cwm + (c - 4 * nq);
+      step = 4;
+      count = kWaves - cwm;
+    } else {
+      first = 4 * cwm + (c - 4 * nq);
+      step = nb;
+      count = 4 * (kWaves - cwm) / nb;
+    }
+    M.red[c] = (uint32_t)first | ((uint32_t)step << 6) | ((uint32_t)count << 12);
+  }
+  int worst = 0;
+  for (int s = 0; s < 4; ++s) {
+    int sum = 0;
+    for (int w = s; w < kWaves; w += 4) sum += (int)(M.wave[w] & 255u);
+    worst = std::max(worst, sum);
+  }
+  return worst;
+}
+
+// Best chunked workgroup for one split of `units` half-groups: Q chunks per workgroup (the launch
+// within one workgroup per compute unit) and the number of main waves with the lowest cost.
+// Returns the cost, or -1 when no Q fits.
+int plan_chunks(const Product* p, int n, int units, int& best_q, int& best_wm) {
+  const int64_t cus = device_cu_count();
+  int best = -1;
+  for (int Q = 1; Q <= 8; ++Q) {
+    int64_t wgs = 0;
+    for (int i = 0; i < n; ++i) wgs += (int64_t)p[i].inst * ceil_div(ceil_div(p[i].d_out, kChunkRows), Q);
+    if (wgs > cus) continue;
+    const int nq = Q >> 2, nb = Q & 3;
+    // main waves: all of them without remaining chunks, none without quads, else at least one
+    // per quad and at least one wave left for the remaining chunks
+    const int lo = nb == 0 ? kWaves : nq, hi = nb == 0 ? kWaves : (nq == 0 ? 0 : kWaves - 1);
+    for (int wm = hi; wm >= lo; --wm) {  // ties: more main waves (one table row per wave)
+      ChunkMap M;
+      const int c = chunk_map(Q, wm, units, M);
+      if (c >= 0 && (best < 0 || c < best)) {
+        best = c;
+        best_q = Q;
+        best_wm = wm;
+      }
+    }
+  }
+  return best;
+}
+
 // Workgroup shape and groups per split of a batch-one launch. With every codebook below 256
 // entries (the tables of K = 256 leave room for 8 groups only), measured on the decoder layer:
 //   1. one split per product when a shape with more parts per tile fits it in one workgroup per
@@ -517,6 +737,8 @@ int plan_gs(const Product* p, int n, int T) {
 // The LDS check assumes the input is staged whole, so the plan does not depend on the pointers.
 void plan_shape(const Product* p, int n, int maxL, bool shapes, Plan& P) {
   P.tiles = 4;
+  P.cq = 0;
+  P.cwm = 0;
   P.gs = plan_gs(p, n, 4);
   if (!shapes || maxL > 7) return;
   const int64_t cus = device_cu_count();
@@ -534,6 +756,24 @@ void plan_shape(const Product* p, int n, int maxL, bool shapes, Plan& P) {
     if (fits(max_ng, T)) {
       P.tiles = T;
       P.gs = max_ng;
+      // The chunked shape (one split as well) when the tile shape leaves a SIMD 16 or more
+      // half-group steps and the chunks cut that down: gate|up goes from 20 steps on 152 compute
+      // units to 13 on 244 (11.3 -> 10.6 us). With fewer steps the extra workgroups cost more
+      // than they save: each stages x and builds the tables of every column, and their weight
+      // streams delay the input reads (q|k|v: 10 steps on 96 units, 7.3 us; 5 on 192, 7.6 us).
+      int q = 0, wm = 0;
+      bool same_ng = true;
+      for (int i = 0; i < n; ++i) same_ng = same_ng && p[i].d_in / kGroupCols == max_ng;
+      const int c = same_ng && max_ng <= shape_max_gs(0) &&
+                            lds_bytes(maxL, max_ng, whole, 0) <= 160 * 1024
+                        ? plan_chunks(p, n, 2 * max_ng, q, wm)
+                        : -1;
+      const int tc = shape_cost(T, 2 * max_ng);
+      if (c >= 0 && tc >= 16 && c < tc) {
+        P.tiles = 0;
+        P.cq = q;
+        P.cwm = wm;
+      }
       return;
     }
   }
@@ -550,7 +790,8 @@ void plan_shape(const Product* p, int n, int maxL, bool shapes, Plan& P) {
 // counts, so the 2-D grid (pieces x workgroups of the widest piece) wastes few workgroups.
 void plan_pieces(const Product* p, int n, int maxL, bool shapes, Plan& P) {
   plan_shape(p, n, maxL, shapes, P);
-  const int kTiles = P.tiles;
+  const bool chunked = P.tiles == 0;
+  const int kTiles = chunked ? 1 : P.tiles;
   int S[kMaxJobs], gs[kMaxJobs], rq[kMaxJobs];
   int64_t count[kMaxJobs];
   int64_t smallest = INT64_MAX;
@@ -559,7 +800,8 @@ void plan_pieces(const Product* p, int n, int maxL, bool shapes, Plan& P) {
     const int g = P.gs < ng ? P.gs : ng;
     S[i] = ceil_div(ng, g);
     gs[i] = ceil_div(ng, S[i]);
-    rq[i] = ceil_div(ceil_div(p[i].d_out, kTileRows), kTiles);
+    rq[i] = chunked ? ceil_div(ceil_div(p[i].d_out, kChunkRows), P.cq)
+                    : ceil_div(ceil_div(p[i].d_out, kTileRows), kTiles);
     count[i] = (int64_t)p[i].inst * rq[i] * S[i];
     if (count[i] < smallest) smallest = count[i];
   }
@@ -587,9 +829,19 @@ void plan_pieces(const Product* p, int n, int maxL, bool shapes, Plan& P) {
       J.d_out = p[i].d_out;
       J.d_in = p[i].d_in;
       J.ng = p[i].d_in / kGroupCols;
-      J.tile0 = q0 * kTiles;
-      J.rt = rt_all - J.tile0 < rq_per * kTiles ? rt_all - J.tile0 : rq_per * kTiles;
-      J.rq = ceil_div(J.rt, kTiles);
+      if (chunked) {
+        const int nch = ceil_div(p[i].d_out, kChunkRows);
+        J.chunk0 = q0 * P.cq;
+        J.nchunk = std::min(nch - J.chunk0, rq_per * P.cq);
+        J.rq = ceil_div(J.nchunk, P.cq);
+        J.cq = P.cq;
+        J.tile0 = 0;
+        J.rt = rt_all;
+      } else {
+        J.tile0 = q0 * kTiles;
+        J.rt = rt_all - J.tile0 < rq_per * kTiles ? rt_all - J.tile0 : rq_per * kTiles;
+        J.rq = ceil_div(J.rt, kTiles);
+      }
       J.S = S[i];
       J.gs = gs[i];
       J.inst = p[i].inst;
@@ -632,6 +884,9 @@ int launch(Plan& P, const Job* proto, bool whole, int maxL, void* ws, size_t ws_
     J.tile0 = plan.tile0;
     J.rt = plan.rt;
     J.rq = plan.rq;
+    J.cq = plan.cq;
+    J.chunk0 = plan.chunk0;
+    J.nchunk = plan.nchunk;
     J.S = plan.S;
     J.gs = plan.gs;
     J.inst = plan.inst;
@@ -671,12 +926,15 @@ int launch(Plan& P, const Job* proto, bool whole, int maxL, void* ws, size_t ws_
     J.consumer_wgs = consumers;
     if (i != first_consumer) J.h_out = nullptr;
   }
+  if (P.tiles == 0 && chunk_map(P.cq, P.cwm, 2 * T.jobs[0].ng, T.cmap) < 0) return SAGE_ERR_ARG;
   const bool fused = signals > 0;
   if (fused && !whole) return SAGE_ERR_ARG;  // the fused block stages its input whole
   if (fused && P.tiles != 4) return SAGE_ERR_ARG;  // the fused block is built for the 4 x 4 shape
   static bool attr_done = false;
   if (!attr_done) {
-    const void* kernels[7] = {reinterpret_cast<const void*>(gemv_kernel<4, true, false>),
+    const void* kernels[9] = {reinterpret_cast<const void*>(gemv_kernel<0, true, false>),
+                              reinterpret_cast<const void*>(gemv_kernel<0, false, false>),
+                              reinterpret_cast<const void*>(gemv_kernel<4, true, false>),
                               reinterpret_cast<const void*>(gemv_kernel<4, false, false>),
                               reinterpret_cast<const void*>(gemv_kernel<4, true, true>),
                               reinterpret_cast<const void*>(gemv_kernel<2, true, false>),
@@ -694,6 +952,9 @@ int launch(Plan& P, const Job* proto, bool whole, int maxL, void* ws, size_t ws_
   const dim3 block(kThreads);
   if (fused) {
     hipLaunchKernelGGL((gemv_kernel<4, true, true>), grid, block, lds, stream, T);
+  } else if (P.tiles == 0) {
+    if (whole) hipLaunchKernelGGL((gemv_kernel<0, true, false>), grid, block, lds, stream, T);
+    else hipLaunchKernelGGL((gemv_kernel<0, false, false>), grid, block, lds, stream, T);
   } else if (P.tiles == 1) {
     if (whole) hipLaunchKernelGGL((gemv_kernel<1, true, false>), grid, block, lds, stream, T);
     else hipLaunchKernelGGL((gemv_kernel<1, false, false>), grid, block, lds, stream, T);

@@ -9,16 +9,23 @@ namespace sage {
 // threads). The parts of a row tile split the workgroup's columns and add their partial sums in
 // LDS. T = 4 is the general shape; T = 2 and T = 1 put more parts on a tile, so fewer workgroups
 // of other compute units have to combine split-K partials (planner in sage_gemv.hip).
+// T = 0 is the chunked shape for unsplit launches: the workgroup owns Q chunks of 16 rows (not
+// tied to 64-row tiles) and each 16-lane group of a wave works on one chunk, so a launch can
+// spread its rows over every compute unit without split-K.
 constexpr int kWaves = 16;
 constexpr int kThreads = kWaves * 64;
+__host__ __device__ constexpr int shape_max_gs(int T) {
+  return T == 4 ? 8 : (T == 2 || T == 0 ? 20 : 24);
+}
 template <int T>
 struct WgShape {
-  static constexpr int kTiles = T;
-  static constexpr int kParts = kWaves / T;
-  static constexpr int kMaxGS = T == 4 ? 8 : (T == 2 ? 20 : 24);           // groups per workgroup
-  static constexpr int kMaxUnits = (2 * kMaxGS + kParts - 1) / kParts;     // half-groups per wave
+  static constexpr int kTiles = T == 0 ? 1 : T;
+  static constexpr int kParts = kWaves / kTiles;
+  static constexpr int kMaxGS = shape_max_gs(T);                              // groups per workgroup
+  static constexpr int kMaxUnits = T == 0 ? 5 : (2 * kMaxGS + kParts - 1) / kParts;  // per wave
 };
-__host__ __device__ constexpr int shape_max_gs(int T) { return T == 4 ? 8 : (T == 2 ? 20 : 24); }
+constexpr int kChunkRows = 16;
+constexpr int kMaxChunkUnits = 5;   // half-groups per lane group in the chunked shape
 constexpr int kMaxJobs = 16;
 constexpr int kWholeXMax = 16384;  // inputs up to this width are staged whole in LDS
 
@@ -46,6 +53,8 @@ struct Job {
   int32_t S, gs;            // column splits and groups per split
   int32_t wg_per_inst, inst;
   int32_t counters_stride;
+  // chunked shape: chunks per workgroup, first chunk and chunks of the piece
+  int32_t cq, chunk0, nchunk;
   // Fused two-stage launches (SwiGLU MLP). A producer piece also writes its rows in fp32 to
   // out32 with coherent stores and signals sync[0] once per finished row group; a consumer piece
   // (src_gate set) waits until sync[0] reaches signal_total, then takes its input from
@@ -60,9 +69,24 @@ struct Job {
   int32_t consumer_wgs;
 };
 
+// Work map of the chunked shape, built by the planner (the same for every piece of a launch).
+//   lane_group[4 w + g]  lane group g of wave w: chunk (bits 0-3), half-groups (bits 4-7), first
+//                        half-group (bits 8-15)
+//   wave[w]              bits 0-7: half-group steps of wave w (its longest lane group); bits
+//                        8-15: lane groups of wave w that share a chunk and add up inside the
+//                        wave first (0 none, 1 g and g + 2, 2 all four)
+//   red[c]               contributors to chunk c after that: lane groups first + i * step for
+//                        i < count (bits 0-5 first, 6-11 step, 12-19 count), added in that order
+struct ChunkMap {
+  uint16_t lane_group[kWaves * 4];
+  uint32_t wave[kWaves];
+  uint32_t red[8];
+};
+
 // Kernel argument: blockIdx.y selects the piece, blockIdx.x the workgroup inside it.
 struct JobTable {
   Job jobs[kMaxJobs];
+  ChunkMap cmap;
 };
 
 static_assert(sizeof(JobTable) <= 4096, "kernel argument block too large");

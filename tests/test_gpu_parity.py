@@ -208,6 +208,29 @@ def test_gemv_split_sweep_full_size(K, V):
     check_gemv(f"sweep 9728x2560 K={K}", c, x, y)
 
 
+@pytest.mark.parametrize("rows,d_in", [((9728, 9731), 2560), ((12000, 11001), 2048),
+                                       ((14000, 13500), 2048)])
+def test_gemv_multi_chunked_rows(rows, d_in):
+    """Two products whose 64-row tiles outnumber the compute units: on a 256-unit device the
+    planner gives each workgroup 5, 6 or 7 chunks of 16 rows (the last with three remaining
+    chunks per workgroup), ragged row counts, two codebook sizes. Repeat calls reproduce the
+    same bits."""
+    import torch
+    rng = W.rng_for(135, rows[0], d_in)
+    cs = [W.draw_codes(rng, rows[0], d_in, 64, 4), W.draw_codes(rng, rows[1], d_in, 128, 3)]
+    x = W.draw_x(rng, (d_in,))
+    ps = [upload_pack(c) for c in cs]
+    xd = torch.from_numpy(x).cuda()
+    ws = sage.workspace(sage.gemv_multi_workspace_bytes(ps), "cuda")
+    ys = sage.gemv_multi(ps, [xd, xd], ws=ws)
+    torch.cuda.synchronize()
+    first = [_np(y).copy() for y in ys]
+    ys = sage.gemv_multi(ps, [xd, xd], ws=ws)
+    for c, y, f in zip(cs, ys, first):
+        check_gemv(f"chunked {c.d_out}x{d_in}", c, x, y)
+        assert np.array_equal(_np(y), f), "repeat call must reproduce the same bits"
+
+
 def test_gemv_workspace_counters_return_to_zero():
     import torch
     c = W.draw_codes(W.rng_for(130), 2560, 9728, 64, 4)  # wide enough to need split-K
