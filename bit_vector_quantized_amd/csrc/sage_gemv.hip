@@ -308,13 +308,19 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, const
               : (tile_ok ? (uint32_t)(ngl * kBlockBytes) : 0u);
   const __amdgpu_buffer_rsrc_t w_rs = view(blk0, w_bytes);
 
-  const u32x4 cw = __builtin_amdgcn_raw_buffer_load_b128(cb_rs, tid * 16, 0, 0);
+  // Waves whose lanes would all read past a small array skip the load (wave-uniform branches):
+  // a load instruction takes the same address-unit time whether or not its lanes are in range.
+  u32x4 cw = {0u, 0u, 0u, 0u};
+  if (wave * 64 < (int)C::kK) cw = __builtin_amdgcn_raw_buffer_load_b128(cb_rs, tid * 16, 0, 0);
   // columns of the workgroup per thread: one for 4 x 4 (8 groups), up to three for the others
   constexpr int kCpt = (WgShape<kT>::kMaxGS * kGroupCols + kThreads - 1) / kThreads;
   uint32_t src[kCpt];
 #pragma unroll
-  for (int k = 0; k < kCpt; ++k)
-    src[k] = __builtin_amdgcn_raw_buffer_load_b32(pi_rs, (tid + k * kThreads) * 4, 0, 0);
+  for (int k = 0; k < kCpt; ++k) {
+    src[k] = 0u;
+    if (wave * 64 + k * kThreads < cols)
+      src[k] = __builtin_amdgcn_raw_buffer_load_b32(pi_rs, (tid + k * kThreads) * 4, 0, 0);
+  }
   __builtin_amdgcn_sched_barrier(0);  // keep the issue order: the counters wait in order
   const uint32_t last = (uint32_t)J.d_in - 1u;  // an out-of-range pi entry is clamped
   // identity when pi is absent, as a lane mask rather than a branch
@@ -327,8 +333,11 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, const
   if constexpr (kWholeX) {
     // the whole activation vector goes to LDS, so the gather x[pi[p]] becomes an LDS read
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i)
-      xc[i] = __builtin_amdgcn_raw_buffer_load_b128(x_rs, (tid + i * kThreads) * 16, 0, 0);
+    for (int i = 0; i < kChunks; ++i) {
+      xc[i] = u32x4{0u, 0u, 0u, 0u};
+      if ((wave * 64 + i * kThreads) * 8 < J.d_in)
+        xc[i] = __builtin_amdgcn_raw_buffer_load_b128(x_rs, (tid + i * kThreads) * 16, 0, 0);
+    }
   } else {
     // wide inputs: the gathered activations straight from memory, after pi
 #pragma unroll
