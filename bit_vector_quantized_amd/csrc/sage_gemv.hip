@@ -237,13 +237,16 @@ __device__ inline void mlp_input(const Job& J, uint16_t* xw, int tid) {
   }
 }
 
-template <int L, int kT, bool kWholeX, bool kFused>
+template <int L, int kT, bool kWholeX, bool kFused, int kMU>
 __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, const ChunkMap& CM,
                                           int inst, int rq, int split, uint8_t* smem) {
   using C = SplitC<L>;
   constexpr int kTiles = WgShape<kT>::kTiles;
   constexpr int kParts = WgShape<kT>::kParts;
-  constexpr int kMaxUnits = WgShape<kT>::kMaxUnits;
+  // half-group steps a wave can take in this launch (the loads of a wave stop there: a load
+  // instruction costs address-unit time even when no lane is in range)
+  constexpr int kMaxUnits = kMU;
+  static_assert(kMU <= WgShape<kT>::kMaxUnits, "more steps than the shape allows");
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: addresses in SGPRs
   const int lane = tid & 63;
@@ -533,7 +536,7 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, const
   if (kFused && J.out32 != nullptr) signal_row_group(J, tid);
 }
 
-template <int kT, bool kWholeX, bool kFused>
+template <int kT, bool kWholeX, bool kFused, int kMU>
 __global__ void __launch_bounds__(kThreads) gemv_kernel(JobTable T) {
   extern __shared__ __align__(16) uint8_t smem[];
   const Job& J = T.jobs[blockIdx.y];
@@ -574,11 +577,11 @@ __global__ void __launch_bounds__(kThreads) gemv_kernel(JobTable T) {
     R.L = J.log2K;
   }
   switch (R.L) {
-    case 4: gemv_body<4, kT, kWholeX, kFused>(R, J, T.cmap, inst, rq, split, smem); break;
-    case 5: gemv_body<5, kT, kWholeX, kFused>(R, J, T.cmap, inst, rq, split, smem); break;
-    case 6: gemv_body<6, kT, kWholeX, kFused>(R, J, T.cmap, inst, rq, split, smem); break;
-    case 7: gemv_body<7, kT, kWholeX, kFused>(R, J, T.cmap, inst, rq, split, smem); break;
-    default: gemv_body<8, kT, kWholeX, kFused>(R, J, T.cmap, inst, rq, split, smem); break;
+    case 4: gemv_body<4, kT, kWholeX, kFused, kMU>(R, J, T.cmap, inst, rq, split, smem); break;
+    case 5: gemv_body<5, kT, kWholeX, kFused, kMU>(R, J, T.cmap, inst, rq, split, smem); break;
+    case 6: gemv_body<6, kT, kWholeX, kFused, kMU>(R, J, T.cmap, inst, rq, split, smem); break;
+    case 7: gemv_body<7, kT, kWholeX, kFused, kMU>(R, J, T.cmap, inst, rq, split, smem); break;
+    default: gemv_body<8, kT, kWholeX, kFused, kMU>(R, J, T.cmap, inst, rq, split, smem); break;
   }
 }
 
@@ -876,6 +879,29 @@ size_t plan_workspace(const Plan& P) {
   return need;
 }
 
+// Kernel variants: shape, whole-x staging, fused stages, and the most half-group steps a wave
+// takes (its loads stop there). The chunked shape comes with 3 to 5 steps, 1 x 16 with 1 to 3,
+// 2 x 8 and 4 x 4 with their maximum.
+typedef void (*GemvFn)(JobTable);
+const GemvFn kGemvFns[] = {
+    gemv_kernel<0, true, false, 3>,  gemv_kernel<0, true, false, 4>,  gemv_kernel<0, true, false, 5>,
+    gemv_kernel<0, false, false, 3>, gemv_kernel<0, false, false, 4>, gemv_kernel<0, false, false, 5>,
+    gemv_kernel<1, true, false, 1>,  gemv_kernel<1, true, false, 2>,  gemv_kernel<1, true, false, 3>,
+    gemv_kernel<1, false, false, 1>, gemv_kernel<1, false, false, 2>, gemv_kernel<1, false, false, 3>,
+    gemv_kernel<2, true, false, 5>,  gemv_kernel<2, false, false, 5>, gemv_kernel<4, true, false, 4>,
+    gemv_kernel<4, false, false, 4>, gemv_kernel<4, true, true, 4>};
+
+GemvFn gemv_fn(int tiles, bool whole, bool fused, int mu) {
+  if (fused) return tiles == 4 && whole && mu <= 4 ? kGemvFns[16] : nullptr;
+  const int w = whole ? 0 : 1;
+  switch (tiles) {
+    case 0: return mu <= 5 ? kGemvFns[w * 3 + std::max(mu, 3) - 3] : nullptr;
+    case 1: return mu <= 3 ? kGemvFns[6 + w * 3 + mu - 1] : nullptr;
+    case 2: return mu <= 5 ? kGemvFns[12 + w] : nullptr;
+    default: return mu <= 4 ? kGemvFns[14 + w] : nullptr;
+  }
+}
+
 // Fills the piece fields the plan leaves open (matrix, vectors, workspace) and launches.
 int launch(Plan& P, const Job* proto, bool whole, int maxL, void* ws, size_t ws_bytes,
            hipStream_t stream) {
@@ -939,41 +965,25 @@ int launch(Plan& P, const Job* proto, bool whole, int maxL, void* ws, size_t ws_
   const bool fused = signals > 0;
   if (fused && !whole) return SAGE_ERR_ARG;  // the fused block stages its input whole
   if (fused && P.tiles != 4) return SAGE_ERR_ARG;  // the fused block is built for the 4 x 4 shape
+  // half-group steps a wave takes at most in this launch
+  int mu = 1;
+  if (P.tiles == 0) {
+    for (int w = 0; w < kWaves; ++w) mu = std::max(mu, (int)(T.cmap.wave[w] & 255u));
+  } else {
+    for (int i = 0; i < P.n; ++i) mu = std::max(mu, ceil_div(2 * T.jobs[i].gs, kWaves / P.tiles));
+  }
+  const GemvFn fn = gemv_fn(P.tiles, whole, fused, mu);
+  if (fn == nullptr) return SAGE_ERR_ARG;
   static bool attr_done = false;
   if (!attr_done) {
-    const void* kernels[9] = {reinterpret_cast<const void*>(gemv_kernel<0, true, false>),
-                              reinterpret_cast<const void*>(gemv_kernel<0, false, false>),
-                              reinterpret_cast<const void*>(gemv_kernel<4, true, false>),
-                              reinterpret_cast<const void*>(gemv_kernel<4, false, false>),
-                              reinterpret_cast<const void*>(gemv_kernel<4, true, true>),
-                              reinterpret_cast<const void*>(gemv_kernel<2, true, false>),
-                              reinterpret_cast<const void*>(gemv_kernel<2, false, false>),
-                              reinterpret_cast<const void*>(gemv_kernel<1, true, false>),
-                              reinterpret_cast<const void*>(gemv_kernel<1, false, false>)};
-    for (const void* k : kernels)
-      if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) !=
-          hipSuccess)
+    for (const GemvFn k : kGemvFns)
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
         return SAGE_ERR_HIP;
     attr_done = true;
   }
   const size_t lds = lds_bytes(maxL, gs_max, whole ? d_in_max : 0, P.tiles);
-  const dim3 grid((unsigned)P.grid_x, (unsigned)P.n);
-  const dim3 block(kThreads);
-  if (fused) {
-    hipLaunchKernelGGL((gemv_kernel<4, true, true>), grid, block, lds, stream, T);
-  } else if (P.tiles == 0) {
-    if (whole) hipLaunchKernelGGL((gemv_kernel<0, true, false>), grid, block, lds, stream, T);
-    else hipLaunchKernelGGL((gemv_kernel<0, false, false>), grid, block, lds, stream, T);
-  } else if (P.tiles == 1) {
-    if (whole) hipLaunchKernelGGL((gemv_kernel<1, true, false>), grid, block, lds, stream, T);
-    else hipLaunchKernelGGL((gemv_kernel<1, false, false>), grid, block, lds, stream, T);
-  } else if (P.tiles == 2) {
-    if (whole) hipLaunchKernelGGL((gemv_kernel<2, true, false>), grid, block, lds, stream, T);
-    else hipLaunchKernelGGL((gemv_kernel<2, false, false>), grid, block, lds, stream, T);
-  } else {
-    if (whole) hipLaunchKernelGGL((gemv_kernel<4, true, false>), grid, block, lds, stream, T);
-    else hipLaunchKernelGGL((gemv_kernel<4, false, false>), grid, block, lds, stream, T);
-  }
+  hipLaunchKernelGGL(fn, dim3((unsigned)P.grid_x, (unsigned)P.n), dim3(kThreads), lds, stream, T);
   return hip_status();
 }
 
