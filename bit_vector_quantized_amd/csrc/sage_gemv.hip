@@ -313,16 +313,41 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, const
 
   // Waves whose lanes would all read past a small array skip the load (wave-uniform branches):
   // a load instruction takes the same address-unit time whether or not its lanes are in range.
+  // With x staged whole its loads go first, so the staging waits for nothing else.
+  constexpr int kChunks = kWholeXMax / 8 / kThreads;  // 16-byte chunks of x per thread
+  u32x4 xc[kChunks];
+  if constexpr (kWholeX) {
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      xc[i] = u32x4{0u, 0u, 0u, 0u};
+      if ((wave * 64 + i * kThreads) * 8 < J.d_in)
+        xc[i] = __builtin_amdgcn_raw_buffer_load_b128(x_rs, (tid + i * kThreads) * 16, 0, 0);
+    }
+  }
   u32x4 cw = {0u, 0u, 0u, 0u};
   if (wave * 64 < (int)C::kK) cw = __builtin_amdgcn_raw_buffer_load_b128(cb_rs, tid * 16, 0, 0);
   // columns of the workgroup per thread: one for 4 x 4 (8 groups), up to three for the others
   constexpr int kCpt = (WgShape<kT>::kMaxGS * kGroupCols + kThreads - 1) / kThreads;
+  // Whole x staged: the tables of subvector position s are written by tps threads, which read
+  // the eight pi entries of s. Otherwise thread t gathers columns t + 1024 k from memory.
+  const int steps = ngl * kSubPerGroup;  // subvector positions of the workgroup
+  const int tps = steps * 2 <= kThreads ? 2 : 1;  // more would repeat the pi loads
+  const int tshift = tps - 1;
+  const int my_step = tid >> tshift;
   uint32_t src[kCpt];
+  u32x4 ps[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+  if constexpr (kWholeX) {
+    if (((wave * 64) >> tshift) < steps) {
+      ps[0] = __builtin_amdgcn_raw_buffer_load_b128(pi_rs, my_step * 32, 0, 0);
+      ps[1] = __builtin_amdgcn_raw_buffer_load_b128(pi_rs, my_step * 32 + 16, 0, 0);
+    }
+  } else {
 #pragma unroll
-  for (int k = 0; k < kCpt; ++k) {
-    src[k] = 0u;
-    if (wave * 64 + k * kThreads < cols)
-      src[k] = __builtin_amdgcn_raw_buffer_load_b32(pi_rs, (tid + k * kThreads) * 4, 0, 0);
+    for (int k = 0; k < kCpt; ++k) {
+      src[k] = 0u;
+      if (wave * 64 + k * kThreads < cols)
+        src[k] = __builtin_amdgcn_raw_buffer_load_b32(pi_rs, (tid + k * kThreads) * 4, 0, 0);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);  // keep the issue order: the counters wait in order
   const uint32_t last = (uint32_t)J.d_in - 1u;  // an out-of-range pi entry is clamped
@@ -330,18 +355,8 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, const
   uint32_t use_pi = R.pi ? ~0u : 0u;
   asm volatile("" : "+v"(use_pi));
   UnitRegs U[kMaxUnits];
-  constexpr int kChunks = kWholeXMax / 8 / kThreads;  // 16-byte chunks of x per thread
-  u32x4 xc[kChunks];
   uint16_t xv[kCpt] = {};
-  if constexpr (kWholeX) {
-    // the whole activation vector goes to LDS, so the gather x[pi[p]] becomes an LDS read
-#pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      xc[i] = u32x4{0u, 0u, 0u, 0u};
-      if ((wave * 64 + i * kThreads) * 8 < J.d_in)
-        xc[i] = __builtin_amdgcn_raw_buffer_load_b128(x_rs, (tid + i * kThreads) * 16, 0, 0);
-    }
-  } else {
+  if constexpr (!kWholeX) {
     // wide inputs: the gathered activations straight from memory, after pi
 #pragma unroll
     for (int k = 0; k < kCpt; ++k) {
@@ -392,26 +407,47 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, const
           *reinterpret_cast<u32x4*>(xw + (tid + i * kThreads) * 8) = xc[i];
     }
     __syncthreads();
+    // the threads of position s gather its eight activations through pi, then write 16 / tps of
+    // its 16 table entries each (no second pass through a gathered copy, one barrier less)
+    if (my_step < steps) {
+      uint32_t h[8];
 #pragma unroll
-    for (int k = 0; k < kCpt; ++k) {
-      const int c = tid + k * kThreads;
-      const uint32_t col = (min(src[k], last) & use_pi) | ((uint32_t)(c0 + c) & ~use_pi);
-      if (c < cols) xp[c] = xw[col];
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t pv = ps[i >> 2][i & 3];
+        const uint32_t col =
+            (min(pv, last) & use_pi) | ((uint32_t)(c0 + my_step * 8 + i) & ~use_pi);
+        h[i] = xw[col];
+      }
+      const uint32_t p01 = h[0] | (h[1] << 16), p23 = h[2] | (h[3] << 16);
+      const uint32_t p45 = h[4] | (h[5] << 16), p67 = h[6] | (h[7] << 16);
+      // thread q of a position writes entries q * np + (i + s) mod np: the eight lanes of one
+      // 128-byte write cycle then land in eight different 16-byte slots (all banks)
+      const int np = 16 >> tshift, q = tid & (tps - 1);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i < np) {
+          const uint32_t n = (uint32_t)(q * np + ((i + my_step) & (np - 1)));
+          const uint2 lo = apply_nibble(p01, p23, n);
+          const uint2 hi = apply_nibble(p45, p67, n);
+          *reinterpret_cast<uint4*>(smem + C::kXtOff + my_step * 256 + n * 16) =
+              make_uint4(lo.x, lo.y, hi.x, hi.y);
+        }
+      }
     }
   } else {
 #pragma unroll
     for (int k = 0; k < kCpt; ++k)
       if (tid + k * kThreads < cols) xp[tid + k * kThreads] = xv[k];
-  }
-  __syncthreads();
-  for (int e = tid; e < ngl * kSubPerGroup * 16; e += kThreads) {
-    const int step = e >> 4;
-    const uint32_t n = (uint32_t)(e & 15);
-    const uint4 v = *reinterpret_cast<const uint4*>(xp + step * 8);
-    const uint2 lo = apply_nibble(v.x, v.y, n);
-    const uint2 hi = apply_nibble(v.z, v.w, n);
-    *reinterpret_cast<uint4*>(smem + C::kXtOff + step * 256 + n * 16) =
-        make_uint4(lo.x, lo.y, hi.x, hi.y);
+    __syncthreads();
+    for (int e = tid; e < ngl * kSubPerGroup * 16; e += kThreads) {
+      const int step = e >> 4;
+      const uint32_t n = (uint32_t)(e & 15);
+      const uint4 v = *reinterpret_cast<const uint4*>(xp + step * 8);
+      const uint2 lo = apply_nibble(v.x, v.y, n);
+      const uint2 hi = apply_nibble(v.z, v.w, n);
+      *reinterpret_cast<uint4*>(smem + C::kXtOff + step * 256 + n * 16) =
+          make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
   }
   __syncthreads();
 
