@@ -92,16 +92,22 @@ struct SplitC {
 __host__ __device__ inline uint32_t lds_tail(int L, int gs) {
   return (L == 8) ? 98304u : (1u << L) * 256u + (uint32_t)gs * kSubPerGroup * 256u;
 }
-// Offsets inside the tail for workgroup shape T (row tiles): gathered columns fp16 [max gs * 128],
-// part sums f32 [parts - 1][T][64] (chunked shape: [16 waves][64]), flag, whole x fp16 [d_in]
-// when staged.
+// Offsets inside the tail for workgroup shape T (row tiles): gathered columns fp16 [max gs * 128]
+// (only when x is not staged whole), part sums f32 [parts - 1][T][64] (chunked shape: [16
+// waves][64]), flag, whole x fp16 [d_in] when staged.
 constexpr uint32_t kTailXp = 0;
-__host__ __device__ constexpr uint32_t tail_red(int T) { return shape_max_gs(T) * kGroupCols * 2; }
+__host__ __device__ constexpr uint32_t tail_red(int T, bool whole) {
+  return whole ? 0u : shape_max_gs(T) * kGroupCols * 2;
+}
 __host__ __device__ constexpr uint32_t red_bytes(int T) {
   return T == 0 ? kWaves * 64 * 4 : (kWaves / T - 1) * T * 64 * 4;
 }
-__host__ __device__ constexpr uint32_t tail_flag(int T) { return tail_red(T) + red_bytes(T); }
-__host__ __device__ constexpr uint32_t tail_x(int T) { return (tail_flag(T) + 16 + 255) / 256 * 256; }
+__host__ __device__ constexpr uint32_t tail_flag(int T, bool whole) {
+  return tail_red(T, whole) + red_bytes(T);
+}
+__host__ __device__ constexpr uint32_t tail_x(int T, bool whole) {
+  return (tail_flag(T, whole) + 16 + 255) / 256 * 256;
+}
 
 struct Resolved {
   const uint8_t* packed;
@@ -295,8 +301,8 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, const
   const int cols = ngl * kGroupCols;
   const uint32_t tail = lds_tail(L, J.gs);
   uint16_t* xp = reinterpret_cast<uint16_t*>(smem + tail + kTailXp);
-  float* red = reinterpret_cast<float*>(smem + tail + tail_red(kT));
-  uint32_t* flag = reinterpret_cast<uint32_t*>(smem + tail + tail_flag(kT));
+  float* red = reinterpret_cast<float*>(smem + tail + tail_red(kT, kWholeX));
+  uint32_t* flag = reinterpret_cast<uint32_t*>(smem + tail + tail_flag(kT, kWholeX));
 
   // 1. Loads, in the order their data is needed.
   const __amdgpu_buffer_rsrc_t cb_rs = view(R.codebook, C::kK * 16u);
@@ -397,7 +403,7 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, const
       *reinterpret_cast<u32x4*>(smem + C::kCbOff + tid * 256 + r * 16) = cw;
   }
   if constexpr (kWholeX) {
-    uint16_t* xw = reinterpret_cast<uint16_t*>(smem + tail + tail_x(kT));
+    uint16_t* xw = reinterpret_cast<uint16_t*>(smem + tail + tail_x(kT, true));
     if (kFused && consumer) {
       mlp_input(J, xw, tid);
     } else {
@@ -652,7 +658,7 @@ int64_t launch_wgs(const Product* p, int n, int gs, int T) {
 size_t lds_bytes(int maxL, int gs, int whole_d_in, int T) {
   size_t need = 0;
   for (int L = 4; L <= maxL; ++L) {
-    const size_t b = lds_tail(L, gs) + tail_x(T);
+    const size_t b = lds_tail(L, gs) + tail_x(T, whole_d_in > 0);
     if (b > need) need = b;
   }
   return need + (size_t)whole_d_in * 2;
@@ -796,10 +802,15 @@ void plan_shape(const Product* p, int n, int maxL, bool shapes, Plan& P) {
     max_din = std::max(max_din, p[i].d_in);
   }
   const int whole = max_din <= kWholeXMax ? max_din : 0;
-  auto fits = [&](int gs, int T) {
-    return gs <= shape_max_gs(T) && launch_wgs(p, n, gs, T) <= cus &&
-           lds_bytes(maxL, gs, whole, T) <= 160 * 1024;
+  // LDS of either input path (whether x is staged whole depends on the pointers at launch)
+  auto lds_ok = [&](int gs, int T) {
+    return std::max(lds_bytes(maxL, gs, whole, T), lds_bytes(maxL, gs, 0, T)) <= 160 * 1024;
   };
+  auto fits = [&](int gs, int T) {
+    return gs <= shape_max_gs(T) && launch_wgs(p, n, gs, T) <= cus && lds_ok(gs, T);
+  };
+  bool same_ng = true;
+  for (int i = 0; i < n; ++i) same_ng = same_ng && p[i].d_in / kGroupCols == max_ng;
   for (int T : {1, 2}) {
     if (fits(max_ng, T)) {
       P.tiles = T;
@@ -810,10 +821,7 @@ void plan_shape(const Product* p, int n, int maxL, bool shapes, Plan& P) {
       // than they save: each stages x and builds the tables of every column, and their weight
       // streams delay the input reads (q|k|v: 10 steps on 96 units, 7.3 us; 5 on 192, 7.6 us).
       int q = 0, wm = 0;
-      bool same_ng = true;
-      for (int i = 0; i < n; ++i) same_ng = same_ng && p[i].d_in / kGroupCols == max_ng;
-      const int c = same_ng && max_ng <= shape_max_gs(0) &&
-                            lds_bytes(maxL, max_ng, whole, 0) <= 160 * 1024
+      const int c = same_ng && max_ng <= shape_max_gs(0) && lds_ok(max_ng, 0)
                         ? plan_chunks(p, n, 2 * max_ng, q, wm)
                         : -1;
       const int tc = shape_cost(T, 2 * max_ng);
@@ -822,6 +830,20 @@ void plan_shape(const Product* p, int n, int maxL, bool shapes, Plan& P) {
         P.cq = q;
         P.cwm = wm;
       }
+      return;
+    }
+  }
+  // No tile shape takes a whole row in one split: the chunked shape still does when its tables
+  // fit (up to 32 groups), which saves the split-K hand-off (o: 160 workgroups of one chunk
+  // instead of 240 split ones).
+  {
+    int q = 0, wm = 0;
+    if (same_ng && max_ng <= shape_max_gs(0) && lds_ok(max_ng, 0) &&
+        plan_chunks(p, n, 2 * max_ng, q, wm) >= 0) {
+      P.tiles = 0;
+      P.gs = max_ng;
+      P.cq = q;
+      P.cwm = wm;
       return;
     }
   }

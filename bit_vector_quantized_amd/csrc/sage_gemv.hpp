@@ -15,7 +15,7 @@ namespace sage {
 constexpr int kWaves = 16;
 constexpr int kThreads = kWaves * 64;
 __host__ __device__ constexpr int shape_max_gs(int T) {
-  return T == 4 ? 8 : (T == 2 || T == 0 ? 20 : 24);
+  return T == 4 ? 8 : (T == 2 ? 20 : (T == 0 ? 32 : 24));
 }
 template <int T>
 struct WgShape {

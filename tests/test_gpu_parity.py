@@ -289,6 +289,27 @@ def test_gemv_input_not_16_byte_aligned():
     check_gemv("x at a 4-byte offset", c, x, y)
 
 
+@pytest.mark.parametrize("aligned", [True, False])
+@pytest.mark.parametrize("K,V", [(64, 4), (16, 6)])
+def test_gemv_one_split_wide_rows(aligned, K, V):
+    """32 column groups in one split (the chunked shape takes whole 4096-wide rows when its
+    tables fit): ragged row count, x staged whole or (at a 4-byte offset) gathered from memory."""
+    import torch
+    rng = W.rng_for(136, K, int(aligned))
+    c = W.draw_codes(rng, 2500, 4096, K, V)
+    x = W.draw_x(rng, (4096,))
+    buf = torch.zeros(4096 + 8, dtype=torch.float16, device="cuda")
+    off = 0 if aligned else 2
+    buf[off:off + 4096] = torch.from_numpy(x).cuda()
+    xd = buf[off:off + 4096]
+    p = upload_pack(c)
+    ws = sage.workspace(sage.gemv_workspace_bytes(p), "cuda")
+    y1 = _np(sage.gemv(p, xd, ws=ws)).copy()
+    y = sage.gemv(p, xd, ws=ws)
+    check_gemv(f"2500x4096 K={K} aligned={aligned}", c, x, y)
+    assert np.array_equal(_np(y), y1)
+
+
 def test_gemv_identity_permutation():
     """pi absent (NULL): columns are taken in stored order."""
     import dataclasses
