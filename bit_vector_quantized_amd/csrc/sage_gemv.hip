@@ -82,15 +82,15 @@ struct SplitC {
   // OR-ing this exponent onto q at bit 8+L gives the float 2^(15-L) + q exactly.
   static constexpr uint32_t kExpo = (127u + 15u - (uint32_t)L) << 23;
   static constexpr float kBias = (float)(1u << (15 - L));
-  // LDS: codebook replicas, then the signed-activation tables (K = 256: tables first, so both
-  // stay inside the first 96 KiB), then the region that lds_tail() describes.
-  static constexpr uint32_t kCbOff = (L == 8) ? 32768u : 0u;
-  static constexpr uint32_t kXtOff = (L == 8) ? 0u : kK * 256u;
+  // LDS: codebook replicas, then the signed-activation tables, then the region that lds_tail()
+  // describes.
+  static constexpr uint32_t kCbOff = 0u;
+  static constexpr uint32_t kXtOff = kK * 256u;
 };
 
 // Start of the LDS tail (gathered columns, part sums, flag, whole x) for split L and gs groups.
 __host__ __device__ inline uint32_t lds_tail(int L, int gs) {
-  return (L == 8) ? 98304u : (1u << L) * 256u + (uint32_t)gs * kSubPerGroup * 256u;
+  return (1u << L) * 256u + (uint32_t)gs * kSubPerGroup * 256u;
 }
 // Offsets inside the tail for workgroup shape T (row tiles): gathered columns fp16 [max gs * 128]
 // (only when x is not staged whole), part sums f32 [parts - 1][T][64] (chunked shape: [16
@@ -780,21 +780,24 @@ int plan_chunks(const Product* p, int n, int units, int& best_q, int& best_wm) {
   return best;
 }
 
-// Workgroup shape and groups per split of a batch-one launch. With every codebook below 256
-// entries (the tables of K = 256 leave room for 8 groups only), measured on the decoder layer:
+// Workgroup shape and groups per split of a batch-one launch (every shape within the LDS: the
+// codebook of the largest split in the launch, the tables of its groups, the staged x), measured
+// on the decoder layer:
 //   1. one split per product when a shape with more parts per tile fits it in one workgroup per
 //      compute unit: 1 x 16 first (q|k|v: 7.56 us against 7.57 us), then 2 x 8 (gate|up: 10.1 us
-//      against 10.5 us);
-//   2. else 1 x 16 with the fewest groups per split that keep one round (o: 7.6 us against 8.4 us,
-//      down: 9.3 us against 10.0 us: a tile's 16 parts leave 6 splits instead of 16 and 19);
-//   3. else the general 4 x 4 shape.
-// The LDS check assumes the input is staged whole, so the plan does not depend on the pointers.
+//      against 10.5 us), or the chunked shape (below);
+//   2. else the chunked shape in one split, when its tables fit;
+//   3. else 1 x 16 with the fewest groups per split that keep one round (down: 9.3 us against
+//      10.0 us: a tile's 16 parts leave 6 splits instead of 19);
+//   4. else the general 4 x 4 shape.
+// The LDS check covers both input paths (x staged whole or gathered from memory), so the plan
+// does not depend on the pointers.
 void plan_shape(const Product* p, int n, int maxL, bool shapes, Plan& P) {
   P.tiles = 4;
   P.cq = 0;
   P.cwm = 0;
   P.gs = plan_gs(p, n, 4);
-  if (!shapes || maxL > 7) return;
+  if (!shapes) return;
   const int64_t cus = device_cu_count();
   int max_ng = 0, max_din = 0;
   for (int i = 0; i < n; ++i) {
@@ -1057,8 +1060,8 @@ using namespace sage;
 
 namespace {
 
-// shapes: whether the batch-one launch may use the 2 x 8 and 1 x 16 workgroup shapes (the
-// fused SwiGLU launch keeps 4 x 4)
+// shapes: whether the launch may use the shapes other than 4 x 4 (the fused SwiGLU launch keeps
+// 4 x 4)
 int multi_plan(const sage_matrix_t* mats, int n, bool shapes, Plan& P) {
   Product p[kMaxJobs];
   int maxL = 4;
@@ -1073,7 +1076,7 @@ int multi_plan(const sage_matrix_t* mats, int n, bool shapes, Plan& P) {
 int moe_plan(const sage_matrix_t* shapes, int n_mats, int n_sel, Plan& P) {
   Product p[kMaxJobs];
   for (int j = 0; j < n_mats; ++j) p[j] = Product{shapes[j].d_out, shapes[j].d_in, n_sel};
-  plan_pieces(p, n_mats, 8, false, P);
+  plan_pieces(p, n_mats, 8, true, P);
   return SAGE_OK;
 }
 
