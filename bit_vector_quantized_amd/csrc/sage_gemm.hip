@@ -252,6 +252,15 @@ __device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint
   u32x4 xc[kVecLoads];
   uint16_t xv[kCpt][kDirectRows];
   const int nck = ngl * (kGroupCols / 8);
+  // gathered path: pi goes out before the weights (it decides the activation addresses)
+  uint32_t pv[kCpt];
+  if constexpr (!kVec) {
+    const __amdgpu_buffer_rsrc_t pi_rs =
+        view(A.pi ? A.pi + c0 : nullptr, A.pi ? (uint32_t)cols * 4u : 0u);
+#pragma unroll
+    for (int q = 0; q < kCpt; ++q)
+      pv[q] = __builtin_amdgcn_raw_buffer_load_b32(pi_rs, (tid + q * kGThreads) * 4, 0, 0);
+  }
   if constexpr (kVec) {
 #pragma unroll
     for (int i = 0; i < kVecLoads; ++i) {
@@ -278,13 +287,10 @@ __device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (!kVec) {
     // few rows in original order: gather through pi straight from X (rows >= mrows read zeros)
-    const __amdgpu_buffer_rsrc_t pi_rs =
-        view(A.pi ? A.pi + c0 : nullptr, A.pi ? (uint32_t)cols * 4u : 0u);
 #pragma unroll
     for (int q = 0; q < kCpt; ++q) {
       const int c = tid + q * kGThreads;
-      const uint32_t pv = __builtin_amdgcn_raw_buffer_load_b32(pi_rs, c * 4, 0, 0);
-      const uint32_t src = A.pi ? min(pv, (uint32_t)A.d_in - 1u) : (uint32_t)(c0 + c);
+      const uint32_t src = A.pi ? min(pv[q], (uint32_t)A.d_in - 1u) : (uint32_t)(c0 + c);
 #pragma unroll
       for (int m = 0; m < kDirectRows; ++m)
         xv[q][m] = __builtin_amdgcn_raw_buffer_load_b16(
@@ -324,9 +330,16 @@ __device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint
   for (int t = 0; t < NT; ++t) acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
   const bool row_ok = tile_ok && wrow < A.d_out;  // padded rows decode to zero weights anyway
   const uint32_t laneoff = (uint32_t)(lane & 15) * 16u;
+  // the SIMD's issue slots go to the oldest wave first; a wave's priority is its remaining groups
+  // (3 down to 0), so the four waves of a SIMD advance together instead of one after another
+  __builtin_amdgcn_s_setprio(3);
 #pragma unroll
   for (int k = 0; k < kGMaxUnits; ++k) {
     if (k < ngp) {
+      const int left = ngp - 1 - k;
+      if (left == 2) __builtin_amdgcn_s_setprio(2);
+      else if (left == 1) __builtin_amdgcn_s_setprio(1);
+      else if (left == 0) __builtin_amdgcn_s_setprio(0);
       const int slot = k0 + k;
       const float mu = h2f(sd[k][1]);
       const float dl = h2f(sd[k][1] >> 16);
@@ -367,6 +380,7 @@ __device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint
     }
   }
 
+  __builtin_amdgcn_s_setprio(0);
   // 4. The other column parts hand their sums to the first through LDS (the X tile is done);
   // part order is kept.
   __syncthreads();
