@@ -381,6 +381,10 @@ def bench_single_products(kind, steps, warmup):
     if kind in ("single", "all"):
         for name, c in W.decoder_layer().mats.items():
             cases.append((f"layer_{name}_{c.d_out}x{c.d_in}", c, None, 1))
+        # an LM-head-sized product (Qwen3 vocabulary x hidden 2560, 109 MB packed): one launch of
+        # several rounds of workgroups
+        c = W.draw_codes(W.rng_for(190), 151936, 2560, 64, 4)
+        cases.append(("lm_head_151936x2560", c, None, 1))
     if kind in ("gemm", "all"):
         for shape in ((9728, 2560), (2560, 9728)):
             for M in (1, 4, 16, 64):

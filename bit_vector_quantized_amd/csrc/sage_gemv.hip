@@ -857,6 +857,19 @@ void plan_shape(const Product* p, int n, int maxL, bool shapes, Plan& P) {
       return;
     }
   }
+  // More rows than one round of workgroups can hold even with splits (an LM-head-sized product):
+  // several rounds of the chunked shape with its largest workgroups (8 chunks, 128 rows), each
+  // building its tables once for more rows, and no split-K.
+  {
+    ChunkMap M;
+    if (same_ng && max_ng <= shape_max_gs(0) && lds_ok(max_ng, 0) &&
+        chunk_map(8, kWaves, 2 * max_ng, M) >= 0) {
+      P.tiles = 0;
+      P.gs = max_ng;
+      P.cq = 8;
+      P.cwm = kWaves;
+    }
+  }
 }
 
 // Cuts the products into pieces of whole tile blocks (P.tiles row tiles) with similar workgroup
