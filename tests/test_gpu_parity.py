@@ -310,6 +310,18 @@ def test_gemv_one_split_wide_rows(aligned, K, V):
     assert np.array_equal(_np(y), y1)
 
 
+def test_gemv_more_rows_than_one_round():
+    """40003 x 1024: more 64-row tiles than one round of workgroups can hold even with splits, so
+    the launch runs several rounds of 128-row chunked workgroups (on a 256-unit device)."""
+    import torch
+    rng = W.rng_for(137)
+    c = W.draw_codes(rng, 40003, 1024, 32, 5)
+    x = W.draw_x(rng, (1024,))
+    p = upload_pack(c)
+    y = sage.gemv(p, torch.from_numpy(x).cuda())
+    check_gemv("40003x1024", c, x, y)
+
+
 def test_gemv_identity_permutation():
     """pi absent (NULL): columns are taken in stored order."""
     import dataclasses
