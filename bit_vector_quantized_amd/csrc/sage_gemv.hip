@@ -243,7 +243,7 @@ __device__ inline void mlp_input(const Job& J, uint16_t* xw, int tid) {
   }
 }
 
-template <int L, int kT, bool kWholeX, bool kFused, int kMU>
+template <int L, int kT, bool kWholeX, bool kFused, int kMU, bool kStream>
 __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, const ChunkMap& CM,
                                           int inst, int rq, int split, uint8_t* smem) {
   using C = SplitC<L>;
@@ -295,8 +295,6 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, const
     un = (int)((e >> 4) & 15u);
     us = (int)((e >> 8) & 255u);
   }
-  const int gchunk = J.chunk0 + rq * J.cq + ck;  // chunk of the matrix (chunked shape)
-  const bool chunk_ok = kT == 0 && ck < J.cq && gchunk < J.chunk0 + J.nchunk;
   const int c0 = g0 * kGroupCols;
   const int cols = ngl * kGroupCols;
   const uint32_t tail = lds_tail(L, J.gs);
@@ -372,18 +370,24 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, const
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (kT == 0) {
-    // lane l: row 16 * gchunk + l % 16, i.e. row (gchunk % 4) * 16 + l % 16 of tile gchunk / 4
-    const uint32_t rin = (uint32_t)((gchunk & 3) * kChunkRows + (lane & 15));
-    const uint32_t tbase = (uint32_t)((gchunk >> 2) * J.ng + g0) * kBlockBytes;
+  // chunked shape: the packed half-groups of this lane group for workgroup block rqb (lane l:
+  // row 16 * chunk + l % 16, i.e. row (chunk % 4) * 16 + l % 16 of tile chunk / 4)
+  auto load_block = [&](UnitRegs (&Ux)[kMaxUnits], int rqb) {
+    const int gc = J.chunk0 + rqb * J.cq + ck;
+    const bool cok = ck < J.cq && gc < J.chunk0 + J.nchunk;
+    const uint32_t rin = (uint32_t)((gc & 3) * kChunkRows + (lane & 15));
+    const uint32_t tbase = (uint32_t)((gc >> 2) * J.ng + g0) * kBlockBytes;
 #pragma unroll
     for (int k = 0; k < kMaxUnits; ++k) {
       const int u = us + k;
       const uint32_t blk = tbase + (uint32_t)(u >> 1) * kBlockBytes;
-      const bool ok = chunk_ok && k < un;
-      load_unit(U[k], w_rs, ok ? blk + ((u & 1) ? kPlaneB : kPlaneA) + rin * 16 : kNowhere,
+      const bool ok = cok && k < un;
+      load_unit(Ux[k], w_rs, ok ? blk + ((u & 1) ? kPlaneB : kPlaneA) + rin * 16 : kNowhere,
                 ok ? blk + kSidePlane + rin * 8 : kNowhere);
     }
+  };
+  if constexpr (kT == 0) {
+    load_block(U, rq);
   } else {
 #pragma unroll
     for (int k = 0; k < kMaxUnits; ++k) {
@@ -460,26 +464,96 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, const
   // 3. Decode and multiply this wave's half-groups. The four waves of a SIMD share its issue
   // slots, which go to the oldest wave first; a wave's priority is its remaining work (3 down to
   // 0), so the waves advance together and the SIMD stays busy until the last one ends.
-  float acc = 0.0f;
   const uint32_t laneoff = (uint32_t)(lane & 15) * 16u;
   const uint32_t expo = C::kExpo;
+  if constexpr (kT == 0) {
+    auto decode_block = [&](const UnitRegs (&Ux)[kMaxUnits]) {
+      float a = 0.0f;
+      __builtin_amdgcn_s_setprio(3);
+#pragma unroll
+      for (int k = 0; k < kMaxUnits; ++k) {
+        if (k < wmax) {
+          // lane groups past their range keep their sum (their unit, clamped into the split,
+          // addresses valid tables; its zero-filled payload is discarded)
+          const uint32_t u = (uint32_t)min(us + k, units - 1);
+          const uint32_t tb = C::kXtOff + (u >> 1) * (kSubPerGroup * 256) + (u & 1) * (8 * 256);
+          const float a2 = half_dot<L>(Ux[k], u & 1, tb, laneoff, expo, a);
+          a = k < un ? a2 : a;
+          const int left = wmax - 1 - k;
+          if (left == 2) __builtin_amdgcn_s_setprio(2);
+          else if (left == 1) __builtin_amdgcn_s_setprio(1);
+          else if (left == 0) __builtin_amdgcn_s_setprio(0);
+        }
+      }
+      __builtin_amdgcn_s_setprio(0);
+      return a;
+    };
+    // The lane groups of a chunk add up in a fixed order, main waves first, then the
+    // remaining-chunk lane groups; thread t sums row t % 16 of chunk t / 16 of block rqb.
+    uint32_t rm = cm_red[0];  // contributors of this thread's chunk
+#pragma unroll
+    for (int q = 1; q < 8; ++q) rm = (tid >> 4) == q ? cm_red[q] : rm;
+    auto reduce_store = [&](float a, int rqb) {
+      if (presum >= 2) a += __shfl_xor(a, 16);
+      if (presum >= 1) a += __shfl_xor(a, 32);
+      red[wave * 64 + lane] = a;
+      __syncthreads();
+      if (tid < J.cq * kChunkRows) {
+        const int c = tid >> 4, r = tid & 15;
+        const int first = (int)(rm & 63u), step = (int)((rm >> 6) & 63u), count = (int)(rm >> 12);
+        // sixteen LDS reads in flight at a time (zero past the last contributor), added as a
+        // fixed pairwise tree
+        float sum = 0.0f;
+        for (int i0 = 0; i0 < count; i0 += 16) {
+          float v[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float t = red[min(first + (i0 + i) * step, 63) * 16 + r];
+            v[i] = i0 + i < count ? t : 0.0f;
+          }
+#pragma unroll
+          for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+            for (int i = 0; i < w; ++i) v[i] = v[2 * i] + v[2 * i + 1];
+          sum += v[0];
+        }
+        const int gc = J.chunk0 + rqb * J.cq + c;
+        const int row = gc * kChunkRows + r;
+        if (gc < J.chunk0 + J.nchunk && row < J.d_out) {
+          uint16_t* yv = J.y + (int64_t)inst * J.y_stride;
+          yv[row] = f2h(sum);
+        }
+      }
+    };
+    if constexpr (!kStream) {
+      reduce_store(decode_block(U), rq);
+    } else {
+      // Persistent workgroups (launches of several rounds): the tables are built once, then the
+      // workgroup takes blocks rq, rq + G, rq + 2G, ... (G workgroups in the launch) with the
+      // next block's weights loading into the other register set while this one decodes.
+      const int G = J.wg_per_inst;
+      UnitRegs V[kMaxUnits];
+      for (int b = rq; b < J.rq; b += 2 * G) {
+        load_block(V, b + G);
+        reduce_store(decode_block(U), b);
+        __syncthreads();  // the part sums of the next block reuse the LDS
+        if (b + G >= J.rq) break;
+        load_block(U, b + 2 * G);
+        reduce_store(decode_block(V), b + G);
+        __syncthreads();
+      }
+    }
+    return;
+  }
+  float acc = 0.0f;
   __builtin_amdgcn_s_setprio(3);
-  const int nloop = kT == 0 ? wmax : nu;
+  const int nloop = nu;
 #pragma unroll
   for (int k = 0; k < kMaxUnits; ++k) {
     if (k < nloop) {
-      if constexpr (kT == 0) {
-        // lane groups past their range keep their sum (their unit, clamped into the split,
-        // addresses valid tables; its zero-filled payload is discarded)
-        const uint32_t u = (uint32_t)min(us + k, units - 1);
-        const uint32_t tb = C::kXtOff + (u >> 1) * (kSubPerGroup * 256) + (u & 1) * (8 * 256);
-        const float a2 = half_dot<L>(U[k], u & 1, tb, laneoff, expo, acc);
-        acc = k < un ? a2 : acc;
-      } else {
-        const uint32_t u = (uint32_t)(u0 + k);
-        const uint32_t tb = C::kXtOff + (u >> 1) * (kSubPerGroup * 256) + (u & 1) * (8 * 256);
-        acc = half_dot<L>(U[k], u & 1, tb, laneoff, expo, acc);
-      }
+      const uint32_t u = (uint32_t)(u0 + k);
+      const uint32_t tb = C::kXtOff + (u >> 1) * (kSubPerGroup * 256) + (u & 1) * (8 * 256);
+      acc = half_dot<L>(U[k], u & 1, tb, laneoff, expo, acc);
       const int left = nloop - 1 - k;
       if (left == 2) __builtin_amdgcn_s_setprio(2);
       else if (left == 1) __builtin_amdgcn_s_setprio(1);
@@ -487,45 +561,6 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, const
     }
   }
   __builtin_amdgcn_s_setprio(0);
-
-  if constexpr (kT == 0) {
-    // Chunked shape (one split): the lane groups of a chunk add up in a fixed order, main waves
-    // first, then the remaining-chunk lane groups; thread t sums row t % 16 of chunk t / 16.
-    if (presum >= 2) acc += __shfl_xor(acc, 16);
-    if (presum >= 1) acc += __shfl_xor(acc, 32);
-    red[wave * 64 + lane] = acc;
-    __syncthreads();
-    if (tid < J.cq * kChunkRows) {
-      const int c = tid >> 4, r = tid & 15;
-      uint32_t rm = cm_red[0];
-#pragma unroll
-      for (int q = 1; q < 8; ++q) rm = c == q ? cm_red[q] : rm;
-      const int first = (int)(rm & 63u), step = (int)((rm >> 6) & 63u), count = (int)(rm >> 12);
-      // sixteen LDS reads in flight at a time (zero past the last contributor), added as a fixed
-      // pairwise tree
-      float sum = 0.0f;
-      for (int i0 = 0; i0 < count; i0 += 16) {
-        float v[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float t = red[min(first + (i0 + i) * step, 63) * 16 + r];
-          v[i] = i0 + i < count ? t : 0.0f;
-        }
-#pragma unroll
-        for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-          for (int i = 0; i < w; ++i) v[i] = v[2 * i] + v[2 * i + 1];
-        sum += v[0];
-      }
-      const int gc = J.chunk0 + rq * J.cq + c;
-      const int row = gc * kChunkRows + r;
-      if (gc < J.chunk0 + J.nchunk && row < J.d_out) {
-        uint16_t* yv = J.y + (int64_t)inst * J.y_stride;
-        yv[row] = f2h(sum);
-      }
-    }
-    return;
-  }
 
   // 4. Column parts of a row tile add up in LDS (in part order).
   if (part > 0) red[((part - 1) * kTiles + tile) * 64 + lane] = acc;
@@ -578,7 +613,7 @@ __device__ __forceinline__ void gemv_body(const Resolved& R, const Job& J, const
   if (kFused && J.out32 != nullptr) signal_row_group(J, tid);
 }
 
-template <int kT, bool kWholeX, bool kFused, int kMU>
+template <int kT, bool kWholeX, bool kFused, int kMU, bool kStream = false>
 __global__ void __launch_bounds__(kThreads) gemv_kernel(JobTable T) {
   extern __shared__ __align__(16) uint8_t smem[];
   const Job& J = T.jobs[blockIdx.y];
@@ -619,11 +654,11 @@ __global__ void __launch_bounds__(kThreads) gemv_kernel(JobTable T) {
     R.L = J.log2K;
   }
   switch (R.L) {
-    case 4: gemv_body<4, kT, kWholeX, kFused, kMU>(R, J, T.cmap, inst, rq, split, smem); break;
-    case 5: gemv_body<5, kT, kWholeX, kFused, kMU>(R, J, T.cmap, inst, rq, split, smem); break;
-    case 6: gemv_body<6, kT, kWholeX, kFused, kMU>(R, J, T.cmap, inst, rq, split, smem); break;
-    case 7: gemv_body<7, kT, kWholeX, kFused, kMU>(R, J, T.cmap, inst, rq, split, smem); break;
-    default: gemv_body<8, kT, kWholeX, kFused, kMU>(R, J, T.cmap, inst, rq, split, smem); break;
+    case 4: gemv_body<4, kT, kWholeX, kFused, kMU, kStream>(R, J, T.cmap, inst, rq, split, smem); break;
+    case 5: gemv_body<5, kT, kWholeX, kFused, kMU, kStream>(R, J, T.cmap, inst, rq, split, smem); break;
+    case 6: gemv_body<6, kT, kWholeX, kFused, kMU, kStream>(R, J, T.cmap, inst, rq, split, smem); break;
+    case 7: gemv_body<7, kT, kWholeX, kFused, kMU, kStream>(R, J, T.cmap, inst, rq, split, smem); break;
+    default: gemv_body<8, kT, kWholeX, kFused, kMU, kStream>(R, J, T.cmap, inst, rq, split, smem); break;
   }
 }
 
@@ -638,6 +673,7 @@ struct Product {
 struct Plan {
   int tiles;              // workgroup shape: row tiles per workgroup (4, 2 or 1; 0 = chunked)
   int cq, cwm;            // chunked shape: chunks per workgroup, waves on whole quads
+  bool stream;            // chunked shape with persistent workgroups (several blocks each)
   int gs;                 // groups per split (before balancing per product)
   int n;                  // pieces
   Job pieces[kMaxJobs];   // planning fields filled: d_out, d_in, tile0, rt, rq, ng, S, gs, inst
@@ -796,6 +832,7 @@ void plan_shape(const Product* p, int n, int maxL, bool shapes, Plan& P) {
   P.tiles = 4;
   P.cq = 0;
   P.cwm = 0;
+  P.stream = false;
   P.gs = plan_gs(p, n, 4);
   if (!shapes) return;
   const int64_t cus = device_cu_count();
@@ -858,12 +895,19 @@ void plan_shape(const Product* p, int n, int maxL, bool shapes, Plan& P) {
     }
   }
   // More rows than one round of workgroups can hold even with splits (an LM-head-sized product):
-  // several rounds of the chunked shape with its largest workgroups (8 chunks, 128 rows), each
-  // building its tables once for more rows, and no split-K.
-  {
+  // one product gets persistent chunked workgroups (one per compute unit, blocks of 2 chunks, the
+  // tables built once, the next block's weights loading while one decodes); several products
+  // get rounds of the chunked shape with its largest workgroups (8 chunks), no split-K either way.
+  if (same_ng && max_ng <= shape_max_gs(0) && lds_ok(max_ng, 0)) {
     ChunkMap M;
-    if (same_ng && max_ng <= shape_max_gs(0) && lds_ok(max_ng, 0) &&
-        chunk_map(8, kWaves, 2 * max_ng, M) >= 0) {
+    const bool single = n == 1 && p[0].inst == 1;
+    if (single && chunk_map(2, 0, 2 * max_ng, M) >= 0 && (M.wave[0] & 255u) <= 2) {
+      P.tiles = 0;
+      P.gs = max_ng;
+      P.cq = 2;
+      P.cwm = 0;
+      P.stream = true;
+    } else if (chunk_map(8, kWaves, 2 * max_ng, M) >= 0) {
       P.tiles = 0;
       P.gs = max_ng;
       P.cq = 8;
@@ -932,6 +976,7 @@ void plan_pieces(const Product* p, int n, int maxL, bool shapes, Plan& P) {
       J.gs = gs[i];
       J.inst = p[i].inst;
       J.wg_per_inst = J.rq * J.S;
+      if (P.stream) J.wg_per_inst = (int)std::min<int64_t>(J.rq, device_cu_count());
       J.partial_stride = J.S > 1 ? (int64_t)J.S * J.rt * kTileRows : 0;
       J.counters_stride = J.S > 1 ? J.rq : 0;
       if (J.wg_per_inst * J.inst > P.grid_x) P.grid_x = J.wg_per_inst * J.inst;
@@ -963,10 +1008,12 @@ const GemvFn kGemvFns[] = {
     gemv_kernel<1, true, false, 1>,  gemv_kernel<1, true, false, 2>,  gemv_kernel<1, true, false, 3>,
     gemv_kernel<1, false, false, 1>, gemv_kernel<1, false, false, 2>, gemv_kernel<1, false, false, 3>,
     gemv_kernel<2, true, false, 5>,  gemv_kernel<2, false, false, 5>, gemv_kernel<4, true, false, 4>,
-    gemv_kernel<4, false, false, 4>, gemv_kernel<4, true, true, 4>};
+    gemv_kernel<4, false, false, 4>, gemv_kernel<4, true, true, 4>,
+    gemv_kernel<0, true, false, 2, true>, gemv_kernel<0, false, false, 2, true>};
 
-GemvFn gemv_fn(int tiles, bool whole, bool fused, int mu) {
+GemvFn gemv_fn(int tiles, bool whole, bool fused, int mu, bool stream) {
   if (fused) return tiles == 4 && whole && mu <= 4 ? kGemvFns[16] : nullptr;
+  if (stream) return tiles == 0 && mu <= 2 ? kGemvFns[whole ? 17 : 18] : nullptr;
   const int w = whole ? 0 : 1;
   switch (tiles) {
     case 0: return mu <= 5 ? kGemvFns[w * 3 + std::max(mu, 3) - 3] : nullptr;
@@ -1046,7 +1093,7 @@ int launch(Plan& P, const Job* proto, bool whole, int maxL, void* ws, size_t ws_
   } else {
     for (int i = 0; i < P.n; ++i) mu = std::max(mu, ceil_div(2 * T.jobs[i].gs, kWaves / P.tiles));
   }
-  const GemvFn fn = gemv_fn(P.tiles, whole, fused, mu);
+  const GemvFn fn = gemv_fn(P.tiles, whole, fused, mu, P.stream);
   if (fn == nullptr) return SAGE_ERR_ARG;
   static bool attr_done = false;
   if (!attr_done) {

@@ -310,16 +310,34 @@ def test_gemv_one_split_wide_rows(aligned, K, V):
     assert np.array_equal(_np(y), y1)
 
 
-def test_gemv_more_rows_than_one_round():
-    """40003 x 1024: more 64-row tiles than one round of workgroups can hold even with splits, so
-    the launch runs several rounds of 128-row chunked workgroups (on a 256-unit device)."""
+@pytest.mark.parametrize("d_in", [1024, 2560])
+def test_gemv_more_rows_than_one_round(d_in):
+    """More 64-row tiles than one round of workgroups can hold even with splits: one product runs
+    on persistent workgroups that take block after block (ragged last block, fewer blocks than
+    some workgroups' stride); repeat calls reproduce the same bits."""
     import torch
-    rng = W.rng_for(137)
-    c = W.draw_codes(rng, 40003, 1024, 32, 5)
-    x = W.draw_x(rng, (1024,))
+    rng = W.rng_for(137, d_in)
+    c = W.draw_codes(rng, 40003 if d_in == 1024 else 17000, d_in, 32, 5)
+    x = W.draw_x(rng, (d_in,))
     p = upload_pack(c)
-    y = sage.gemv(p, torch.from_numpy(x).cuda())
-    check_gemv("40003x1024", c, x, y)
+    xd = torch.from_numpy(x).cuda()
+    y1 = _np(sage.gemv(p, xd)).copy()
+    y = sage.gemv(p, xd)
+    check_gemv(f"{c.d_out}x{d_in}", c, x, y)
+    assert np.array_equal(_np(y), y1)
+
+
+def test_gemv_multi_more_rows_than_one_round():
+    """Two such products in one launch: rounds of 128-row chunked workgroups."""
+    import torch
+    rng = W.rng_for(138)
+    cs = [W.draw_codes(rng, 20011, 1024, 64, 4), W.draw_codes(rng, 20000, 1024, 16, 6)]
+    x = W.draw_x(rng, (1024,))
+    ps = [upload_pack(c) for c in cs]
+    xd = torch.from_numpy(x).cuda()
+    ys = sage.gemv_multi(ps, [xd, xd], ws=sage.workspace(sage.gemv_multi_workspace_bytes(ps), "cuda"))
+    for c, y in zip(cs, ys):
+        check_gemv(f"multi {c.d_out}x1024", c, x, y)
 
 
 def test_gemv_identity_permutation():
