@@ -895,17 +895,34 @@ void plan_shape(const Product* p, int n, int maxL, bool shapes, Plan& P) {
     }
   }
   // More rows than one round of workgroups can hold even with splits (an LM-head-sized product):
-  // one product gets persistent chunked workgroups (one per compute unit, blocks of 2 chunks, the
-  // tables built once, the next block's weights loading while one decodes); several products
-  // get rounds of the chunked shape with its largest workgroups (8 chunks), no split-K either way.
+  // one product gets persistent chunked workgroups (one per compute unit, the tables built once,
+  // the next block's weights loading while one decodes) with the most chunks a block can take
+  // at two half-group steps per wave (2560-wide rows: 3 chunks, 120 of 128 lane-group steps
+  // used; 2 chunks used 80); several products get rounds of the chunked shape with its largest
+  // workgroups (8 chunks), no split-K either way.
   if (same_ng && max_ng <= shape_max_gs(0) && lds_ok(max_ng, 0)) {
     ChunkMap M;
-    const bool single = n == 1 && p[0].inst == 1;
-    if (single && chunk_map(2, 0, 2 * max_ng, M) >= 0 && (M.wave[0] & 255u) <= 2) {
+    int sq = 0, swm = 0;
+    if (n == 1 && p[0].inst == 1) {
+      for (int Q = 8; Q >= 2 && sq == 0; --Q) {
+        const int nq = Q >> 2, nb = Q & 3;
+        const int lo = nb == 0 ? kWaves : nq, hi = nb == 0 ? kWaves : (nq == 0 ? 0 : kWaves - 1);
+        for (int wm = hi; wm >= lo && sq == 0; --wm) {
+          if (chunk_map(Q, wm, 2 * max_ng, M) < 0) continue;
+          int longest = 0;
+          for (int w = 0; w < kWaves; ++w) longest = std::max(longest, (int)(M.wave[w] & 255u));
+          if (longest <= kStreamSteps) {
+            sq = Q;
+            swm = wm;
+          }
+        }
+      }
+    }
+    if (sq > 0) {
       P.tiles = 0;
       P.gs = max_ng;
-      P.cq = 2;
-      P.cwm = 0;
+      P.cq = sq;
+      P.cwm = swm;
       P.stream = true;
     } else if (chunk_map(8, kWaves, 2 * max_ng, M) >= 0) {
       P.tiles = 0;
@@ -1009,11 +1026,11 @@ const GemvFn kGemvFns[] = {
     gemv_kernel<1, false, false, 1>, gemv_kernel<1, false, false, 2>, gemv_kernel<1, false, false, 3>,
     gemv_kernel<2, true, false, 5>,  gemv_kernel<2, false, false, 5>, gemv_kernel<4, true, false, 4>,
     gemv_kernel<4, false, false, 4>, gemv_kernel<4, true, true, 4>,
-    gemv_kernel<0, true, false, 2, true>, gemv_kernel<0, false, false, 2, true>};
+    gemv_kernel<0, true, false, kStreamSteps, true>, gemv_kernel<0, false, false, kStreamSteps, true>};
 
 GemvFn gemv_fn(int tiles, bool whole, bool fused, int mu, bool stream) {
   if (fused) return tiles == 4 && whole && mu <= 4 ? kGemvFns[16] : nullptr;
-  if (stream) return tiles == 0 && mu <= 2 ? kGemvFns[whole ? 17 : 18] : nullptr;
+  if (stream) return tiles == 0 && mu <= kStreamSteps ? kGemvFns[whole ? 17 : 18] : nullptr;
   const int w = whole ? 0 : 1;
   switch (tiles) {
     case 0: return mu <= 5 ? kGemvFns[w * 3 + std::max(mu, 3) - 3] : nullptr;

@@ -26,6 +26,7 @@ struct WgShape {
 };
 constexpr int kChunkRows = 16;
 constexpr int kMaxChunkUnits = 5;   // half-groups per lane group in the chunked shape
+constexpr int kStreamSteps = 2;     // half-group steps per wave and block of the persistent shape
 constexpr int kMaxJobs = 16;
 constexpr int kWholeXMax = 16384;  // inputs up to this width are staged whole in LDS
 

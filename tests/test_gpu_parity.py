@@ -310,14 +310,15 @@ def test_gemv_one_split_wide_rows(aligned, K, V):
     assert np.array_equal(_np(y), y1)
 
 
-@pytest.mark.parametrize("d_in", [1024, 2560])
+@pytest.mark.parametrize("d_in", [1024, 2560, 4096])
 def test_gemv_more_rows_than_one_round(d_in):
     """More 64-row tiles than one round of workgroups can hold even with splits: one product runs
     on persistent workgroups that take block after block (ragged last block, fewer blocks than
-    some workgroups' stride); repeat calls reproduce the same bits."""
+    some workgroups' stride; blocks of 8, 3 and 2 chunks for 1024-, 2560- and 4096-wide rows);
+    repeat calls reproduce the same bits."""
     import torch
     rng = W.rng_for(137, d_in)
-    c = W.draw_codes(rng, 40003 if d_in == 1024 else 17000, d_in, 32, 5)
+    c = W.draw_codes(rng, {1024: 40003, 2560: 33100, 4096: 16600}[d_in], d_in, 32, 5)
     x = W.draw_x(rng, (d_in,))
     p = upload_pack(c)
     xd = torch.from_numpy(x).cuda()
