@@ -54,8 +54,9 @@ def parse():
                     choices=["layer", "sweep", "gemm", "prefill", "moe", "encode", "single", "all"])
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--fused", action="store_true",
-                    help="run the SwiGLU block as one sage_mlp launch (3 launches per step)")
+    ap.add_argument("--mode", default="compiled", choices=["compiled", "eager"],
+                    help="compiled: inputs arrive permuted, matrices run with pi = NULL (the "
+                         "paper's compiled decoding); eager: each launch gathers through pi")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--eager", action="store_true", help="launch from Python (no graph)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -129,20 +130,29 @@ def load_traffic(name):
 # ------------------------------------------------------------------------------------------------
 
 class LayerBench:
-    """The layer step: q|k|v in one launch, o, then the SwiGLU block. Unfused (default): gate|up
-    in one launch and down on the synthetic intermediate vector (two launches). Fused: one
-    sage_mlp launch for gate, up, silu*mul and down."""
-    UNFUSED = (("qkv", ("q", "k", "v"), "attn_in"), ("o", ("o",), "attn_out"),
-               ("gateup", ("gate", "up"), "mlp_in"), ("down", ("down",), "mlp_mid"))
+    """The layer step: q|k|v in one launch, o, gate|up in one launch, down (4 launches). Mode
+    "compiled": the matrices run with pi = NULL and their inputs arrive already permuted, as the
+    producers of the paper's compiled decoding write them (§3.5); mode "eager": each launch
+    gathers its input through pi itself."""
+    LAUNCHES = (("qkv", ("q", "k", "v"), "attn_in"), ("o", ("o",), "attn_out"),
+                ("gateup", ("gate", "up"), "mlp_in"), ("down", ("down",), "mlp_mid"))
 
-    def __init__(self, copies, steps, fused=False):
+    def __init__(self, copies, steps, mode="compiled"):
+        import dataclasses
+        import numpy as np
         import torch
         import workloads as W
         import bit_vector_quantized_amd as sage
         self.sage = sage
-        self.fused = fused
+        self.mode = mode
         self.layer = W.decoder_layer()
         base = {n: upload_pack(c) for n, c in self.layer.mats.items()}
+        xs = dict(self.layer.xs)
+        if mode == "compiled":
+            for key, names, inp in self.LAUNCHES:
+                pi = self.layer.mats[names[0]].pi
+                xs[inp] = np.ascontiguousarray(xs[inp][pi])
+            base = {n: dataclasses.replace(p, pi=None) for n, p in base.items()}
         self.bytes_per_layer = sum(packed_weight_bytes(p) for p in base.values())
         if copies <= 0:
             need = max(2, math.ceil(2 * MALL_BYTES / self.bytes_per_layer) + 1)
@@ -150,57 +160,29 @@ class LayerBench:
             copies = divisors[0] if divisors else need
         self.copies = [base] + [{n: clone_packed(p) for n, p in base.items()}
                                 for _ in range(copies - 1)]
-        self.xs = {k: torch.from_numpy(v).cuda() for k, v in self.layer.xs.items()}
+        self.xs = {k: torch.from_numpy(v).cuda() for k, v in xs.items()}
         self.ys = {n: torch.empty(p.d_out, dtype=torch.float16, device="cuda")
                    for n, p in base.items()}
-        self.ws = {}
-        for key, names, _ in self.UNFUSED:
-            ps = [base[n] for n in names]
-            self.ws[key] = sage.workspace(sage.gemv_multi_workspace_bytes(ps), "cuda")
-        self.ws["mlp"] = sage.workspace(
-            sage.mlp_workspace_bytes(base["gate"], base["up"], base["down"]), "cuda")
-        if fused:
-            self.dom_name = "mlp (gate|up 2 x 9728x2560, silu*mul, down 2560x9728 in one launch)"
-            # packed fields, codebooks and permutations of the three matrices, x once, y once
-            self.dom_bytes = sum(algorithmic_bytes(base[n]) - base[n].d_in * 2 - base[n].d_out * 2
-                                 for n in ("gate", "up", "down")) \
-                + base["gate"].d_in * 2 + base["down"].d_out * 2
-            self.launches = 3
-            self.dom_profile = "mlp_qwen3_4b_9728x2560"
-        else:
-            self.dom_name = "gemv_kernel (gate|up, 2 x 9728x2560 in one launch)"
-            self.dom_bytes = sum(algorithmic_bytes(base[n]) for n in ("gate", "up"))
-            self.launches = 4
-            self.dom_profile = "gemv_gateup_9728x2560x2"
+        self.dom_name = "gemv_kernel (gate|up, 2 x 9728x2560 in one launch)"
+        self.dom_bytes = sum(algorithmic_bytes(base[n]) for n in ("gate", "up"))
+        self.launches = 4
+        self.dom_profile = "gemv_gateup_9728x2560x2"
+        self.base = base
         torch.cuda.synchronize()
 
-    def dominant(self, i):
+    def launch(self, key, i):
+        names, inp = {k: (n, x) for k, n, x in self.LAUNCHES}[key]
         mats = self.copies[i % len(self.copies)]
-        if self.fused:
-            self.sage.mlp(mats["gate"], mats["up"], mats["down"], self.xs["mlp_in"],
-                          self.ys["down"], ws=self.ws["mlp"])
-        else:
-            x = self.xs["mlp_in"]
-            self.sage.gemv_multi([mats["gate"], mats["up"]], [x, x],
-                                 [self.ys["gate"], self.ys["up"]], ws=self.ws["gateup"])
+        ps = [mats[n] for n in names]
+        x = self.xs[inp]
+        self.sage.gemv_multi(ps, [x] * len(ps), [self.ys[n] for n in names])
+
+    def dominant(self, i):
+        self.launch("gateup", i)
 
     def step(self, i, ev=None):
-        mats = self.copies[i % len(self.copies)]
-        order = self.UNFUSED[:2] if self.fused else self.UNFUSED
-        for key, names, inp in order:
-            ps = [mats[n] for n in names]
-            x = self.xs[inp]
-            if ev is not None and key == "gateup":
-                ev[0].record()
-            self.sage.gemv_multi(ps, [x] * len(ps), [self.ys[n] for n in names], ws=self.ws[key])
-            if ev is not None and key == "gateup":
-                ev[1].record()
-        if self.fused:
-            if ev is not None:
-                ev[0].record()
-            self.dominant(i)
-            if ev is not None:
-                ev[1].record()
+        for key, _, _ in self.LAUNCHES:
+            self.launch(key, i)
 
 
 def timed_graph(bench, steps, warmup, eager=False, dominant=True):
@@ -253,10 +235,10 @@ def timed_graph(bench, steps, warmup, eager=False, dominant=True):
     return t1 - t0, durs
 
 
-def dominant_graph(bench, count, evs):
-    """Average duration of the dominant launch: a graph of `count` such launches over distinct
-    weight copies, replayed between two HIP events on the stream the kernels run on. The figure
-    includes the short gap between consecutive kernels of a graph."""
+def dominant_graph(bench, count, evs, key="gateup"):
+    """Average duration of one launch kind (the dominant gate|up by default): a graph of `count`
+    such launches over distinct weight copies, replayed between two HIP events on the stream the
+    kernels run on. The figure includes the short gap between consecutive kernels of a graph."""
     import torch
     del evs
     s = torch.cuda.Stream()
@@ -265,7 +247,7 @@ def dominant_graph(bench, count, evs):
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
             for i in range(count):
-                bench.dominant(i)
+                bench.launch(key, i)
     torch.cuda.synchronize()
     reps = 10
     with torch.cuda.stream(s):
@@ -503,35 +485,53 @@ def bench_moe(steps, warmup):
     yg = torch.empty((k, W.MOE_INTER), dtype=torch.float16, device="cuda")
     yu = torch.empty_like(yg)
     yd = torch.empty((k, W.MOE_HIDDEN), dtype=torch.float16, device="cuda")
-    shapes = [(W.MOE_INTER, W.MOE_HIDDEN)] * 2 + [(W.MOE_HIDDEN, W.MOE_INTER)]
-    ws = sage.workspace(sage.moe_gemv_workspace_bytes(shapes, k), "cuda")
-    fn = lambda t: sage.moe_gemv(t, 128, shapes, ids, [x, x, h], [0, 0, W.MOE_INTER],
-                                 [yg, yu, yd], [W.MOE_INTER, W.MOE_INTER, W.MOE_HIDDEN], ws=ws)
-    for i in range(warmup):
-        fn(tables[i % copies])
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        with torch.cuda.graph(g, stream=s):
-            for i in range(copies):
-                fn(tables[i])
-    g.replay()
-    torch.cuda.synchronize()
-    reps = max(1, steps // copies)
-    t0 = time.perf_counter()
-    for _ in range(reps):
+    ID, IH = W.MOE_INTER, W.MOE_HIDDEN
+    # tables: gate|up pairs and down per copy (the layer as it runs: two launches, since down
+    # reads silu(gate) * up), and all three per copy (one grouped launch, down on synthetic h)
+    gu = [sage.expert_table([[ex[0], ex[1]] for ex in cp], "cuda")[0] for cp in copy_packs]
+    dn = [sage.expert_table([ex[2] for ex in cp], "cuda")[0] for cp in copy_packs]
+
+    def two_launches(i):
+        sage.moe_gemv_grouped(gu[i], ids, [x, x], [0, 0], [yg.view(-1), yu.view(-1)], [ID, ID])
+        sage.moe_gemv(dn[i], ids, h.view(-1), ID, yd.view(-1), IH)
+
+    def one_launch(i):
+        sage.moe_gemv_grouped(tables[i], ids, [x, x, h.view(-1)], [0, 0, ID],
+                              [yg.view(-1), yu.view(-1), yd.view(-1)], [ID, ID, IH])
+
+    def timed(fn):
+        for i in range(warmup):
+            fn(i % copies)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(copies):
+                    fn(i)
         g.replay()
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / (reps * copies)
+        torch.cuda.synchronize()
+        reps = max(1, steps // copies)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / (reps * copies)
+
+    dt2 = timed(two_launches)
+    dt1 = timed(one_launch)
     routed = [packs[int(e)] for e in moe.ids]
     pb = sum(packed_weight_bytes(p) for ex in routed for p in ex)
     alg = sum(algorithmic_bytes(p) for ex in routed for p in ex)
-    line = {"workload": "moe_qwen3_30b_a3b_top8_of_128", "us_per_call": round(dt * 1e6, 3),
-            "packed_gbs": round(pb / dt / 1e9, 1), "effective_gbs": round(alg / dt / 1e9, 1),
-            "pct_hbm_peak": round(100 * alg / dt / 1e9 / HBM_PEAK_GBS, 1),
-            "tokens_per_s": round(1.0 / dt, 1), "copies": copies}
+    line = {"workload": "moe_qwen3_30b_a3b_top8_of_128",
+            "us_per_layer_two_launches": round(dt2 * 1e6, 3),
+            "us_per_call_one_grouped_launch": round(dt1 * 1e6, 3),
+            "packed_gbs_one_launch": round(pb / dt1 / 1e9, 1),
+            "effective_gbs_one_launch": round(alg / dt1 / 1e9, 1),
+            "pct_hbm_peak_one_launch": round(100 * alg / dt1 / 1e9 / HBM_PEAK_GBS, 1),
+            "packed_gbs_two_launches": round(pb / dt2 / 1e9, 1),
+            "tokens_per_s": round(1.0 / dt2, 1), "copies": copies}
     print(json.dumps(line), flush=True)
     return line
 
@@ -569,25 +569,28 @@ def main():
         log("[bench] calibration copy: 268435456 bytes read, 268435456 bytes written")
         del src, dst
     log("[bench] building the decoder layer copies")
-    bench = LayerBench(args.copies, args.steps, fused=args.fused)
+    bench = LayerBench(args.copies, args.steps, mode=args.mode)
     log(f"[bench] {len(bench.copies)} copies x {bench.bytes_per_layer} packed bytes; "
-        f"timing {args.steps} steps after {args.warmup} warmup steps")
-    # the same layer with the SwiGLU block run the other way, for comparison
-    bench.fused = not args.fused
-    alt_wall, _ = timed_graph(bench, args.steps, args.warmup, eager=args.eager, dominant=False)
-    alt_ms = alt_wall * 1e3 / args.steps
-    bench.fused = args.fused
+        f"timing {args.steps} steps after {args.warmup} warmup steps ({args.mode} decoding)")
     wall, durs = timed_graph(bench, args.steps, args.warmup, eager=args.eager)
     ms_per_step = wall * 1e3 / args.steps
     value = bench.bytes_per_layer / (ms_per_step * 1e-3) / 1e9
     dom_ms = sum(durs) / len(durs) if durs else None
+    launch_us = {k: round(dominant_graph(bench, len(bench.copies), None, k)[0] * 1e3, 3)
+                 for k, _, _ in LayerBench.LAUNCHES}
+    other = LayerBench(args.copies, args.steps, mode="eager" if args.mode == "compiled" else "compiled")
+    other_wall, _ = timed_graph(other, args.steps, args.warmup, dominant=False)
+    other_ms = other_wall * 1e3 / args.steps
+    other_launch_us = {k: round(dominant_graph(other, len(other.copies), None, k)[0] * 1e3, 3)
+                       for k, _, _ in LayerBench.LAUNCHES}
+    del other
     roofline = None
     if dom_ms:
         achieved = bench.dom_bytes / (dom_ms * 1e-3) / 1e9
         roofline = {"kernel": bench.dom_name,
                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": load_traffic(bench.dom_profile),
+                    "traffic": load_traffic(bench.dom_profile + "_" + args.mode),
                     "avg_launch_us": round(dom_ms * 1e3, 3),
                     "algorithmic_bytes_per_launch": bench.dom_bytes}
     line = {
@@ -598,11 +601,16 @@ def main():
         "data": "synthetic",
         "config": {"workload": "qwen3_4b_decoder_layer_batch1", "split_K_V": [64, 4],
                    "matrices": 7, "launches_per_step": bench.launches,
-                   "swiglu_block": "fused (sage_mlp)" if bench.fused else "two launches",
+                   "decoding": args.mode,
                    "packed_bytes_per_step": bench.bytes_per_layer,
-                   "weight_copies": len(bench.copies), "timing": "eager" if args.eager else "hip_graph",
-                   ("unfused_ms_per_step" if bench.fused else "fused_mlp_ms_per_step"):
-                       round(alt_ms, 5)},
+                   "weight_copies": len(bench.copies),
+                   "timing": "eager" if args.eager else "hip_graph",
+                   "launch_us": launch_us,
+                   "source_digest": sage.source_digest(),
+                   ("eager" if args.mode == "compiled" else "compiled") + "_decoding": {
+                       "ms_per_step": round(other_ms, 5),
+                       "packed_gbs": round(bench.bytes_per_layer / (other_ms * 1e-3) / 1e9, 1),
+                       "launch_us": other_launch_us}},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(1e3 / ms_per_step, 1),
         "roofline": roofline,

@@ -52,6 +52,7 @@ _PI64 = ctypes.POINTER(ctypes.c_int64)
 _SIGNATURES = {
     "sage_status_string": (ctypes.c_char_p, [_I]),
     "sage_version": (_I, []),
+    "sage_source_digest": (ctypes.c_char_p, []),
     "sage_format_version": (_I, []),
     "sage_packed_bytes": (_I, [_I, _I, _I, _I, _PSZ]),
     "sage_pack": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
@@ -63,11 +64,9 @@ _SIGNATURES = {
     "sage_gemv_multi": (_I, [_PM, _PP, _PP, _I, _P, _SZ, _P]),
     "sage_gemm_small_workspace_bytes": (_I, [_PM, _I, _PSZ]),
     "sage_gemm_small": (_I, [_PM, _P, _I, _I, _P, _I, _P, _SZ, _P]),
-    "sage_moe_gemv_workspace_bytes": (_I, [_PM, _I, _I, _PSZ]),
-    "sage_moe_gemv": (_I, [_PM, _I, _PM, _I, _P, _I, _PP, _PI64, _PP, _PI64, _P, _SZ, _P]),
+    "sage_moe_gemv": (_I, [_PM, _I, _P, _I, _P, ctypes.c_int64, _P, ctypes.c_int64, _P]),
+    "sage_moe_gemv_grouped": (_I, [_PM, _I, _I, _P, _I, _PP, _PI64, _PP, _PI64, _P]),
     "sage_stream_read": (_I, [_P, _SZ, _P, _P]),
-    "sage_mlp_workspace_bytes": (_I, [_PM, _PM, _PM, ctypes.POINTER(ctypes.c_size_t)]),
-    "sage_mlp": (_I, [_PM, _PM, _PM, _P, _P, _P, _P, _SZ, _P]),
     "sage_encode_fields": (_I, [_P, _I, _I, ctypes.c_int64, _P, _P, _P, _I, _I,
                                 _P, _P, _P, _P, _P, _P, _P]),
     "sage_abs_score_workspace_bytes": (_I, [_I, _I, _PSZ]),
@@ -101,6 +100,11 @@ def header_functions() -> List[str]:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(sage_\w+)\s*\(", text, flags=re.M)))
+
+
+def source_digest() -> str:
+    """sha256 prefix of the sources the loaded libsage.so was built from."""
+    return lib().sage_source_digest().decode()
 
 
 def status_string(status: int) -> str:
@@ -140,6 +144,31 @@ def _require_cuda(*ts):
             raise ValueError("libsage arguments must be device tensors")
 
 
+def _require_vec(name: str, t, n: int, dtype_name: str = "float16"):
+    """t must be a contiguous device tensor of the given dtype with at least n elements."""
+    _require_cuda(t)
+    if str(t.dtype) != "torch." + dtype_name:
+        raise ValueError(f"{name} must be {dtype_name}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < n:
+        raise ValueError(f"{name} has {t.numel()} elements, needs at least {n}")
+
+
+def _check_packed(p) -> None:
+    """The matrix's own buffers match its shape and split (what the kernels will address)."""
+    _require_vec("codebook", p.codebook, 8 * p.K)
+    if p.codebook.numel() != 8 * p.K:
+        raise ValueError(f"codebook must hold exactly {p.K} x 8 values")
+    if p.pi is not None:
+        _require_vec("pi", p.pi, p.d_in, "int32")
+        if p.pi.numel() != p.d_in:
+            raise ValueError(f"pi must hold exactly d_in = {p.d_in} entries")
+    need = packed_bytes(p.d_out, p.d_in, p.log2K, p.V)
+    if p.packed.numel() * p.packed.element_size() < need:
+        raise ValueError(f"packed buffer holds fewer than {need} bytes")
+
+
 @dataclass
 class Packed:
     """A packed matrix resident on the device (owns its buffers)."""
@@ -174,6 +203,13 @@ def pack(signs, idx, rcode, mu, delta, codebook, pi, log2K: int, V: int, stream=
     _require_cuda(signs, idx, rcode, mu, delta, codebook, pi)
     d_out, m = signs.shape
     d_in = m * 8
+    for name, t in (("signs", signs), ("idx", idx), ("rcode", rcode)):
+        if tuple(t.shape) != (d_out, m) or str(t.dtype) != "torch.uint8" or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous uint8 [{d_out}, {m}] tensor")
+    for name, t in (("mu", mu), ("delta", delta)):
+        if (tuple(t.shape) != (d_out, d_in // 128) or str(t.dtype) != "torch.float16"
+                or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float16 [{d_out}, {d_in // 128}] tensor")
     buf = torch.empty(packed_bytes(d_out, d_in, log2K, V), dtype=torch.uint8, device=signs.device)
     _check("sage_pack", lib().sage_pack(_ptr(signs), _ptr(idx), _ptr(rcode), _ptr(mu), _ptr(delta),
                                         d_out, d_in, log2K, V, _ptr(buf), _stream(stream)))
@@ -272,9 +308,12 @@ def silu_mul_permute(G, U, pi=None, out=None, stream=None):
 
 
 def dequant(p: Packed, out=None, stream=None):
+    """Dense fp16 copy of the decoded weights in original column order (see sage_dequant)."""
     torch = _torch()
+    _check_packed(p)
     w = torch.empty((p.d_out, p.d_in), dtype=torch.float16, device=p.packed.device) \
         if out is None else out
+    _require_vec("out", w, p.d_out * p.d_in)
     d = p.desc()
     _check("sage_dequant", lib().sage_dequant(ctypes.byref(d), _ptr(w), _stream(stream)))
     return w
@@ -294,15 +333,17 @@ def workspace(nbytes: int, device):
 
 
 def gemv(p: Packed, x, y=None, ws=None, stream=None):
+    """y = W_hat x (batch one). x in original channel order, or in stored order when p.pi is
+    None (see sage_gemv in include/sage.h)."""
     torch = _torch()
-    _require_cuda(x)
+    _check_packed(p)
+    _require_vec("x", x, p.d_in)
     if y is None:
         y = torch.empty(p.d_out, dtype=torch.float16, device=x.device)
-    if ws is None:
-        ws = workspace(gemv_workspace_bytes(p), x.device)
+    _require_vec("y", y, p.d_out)
     d = p.desc()
-    _check("sage_gemv", lib().sage_gemv(ctypes.byref(d), _ptr(x), _ptr(y), _ptr(ws), ws.numel(),
-                                        _stream(stream)))
+    _check("sage_gemv", lib().sage_gemv(ctypes.byref(d), _ptr(x), _ptr(y), _ptr(ws),
+                                        0 if ws is None else ws.numel(), _stream(stream)))
     return y
 
 
@@ -322,15 +363,21 @@ def gemv_multi_workspace_bytes(ps: Sequence[Packed]) -> int:
 
 
 def gemv_multi(ps: Sequence[Packed], xs, ys=None, ws=None, stream=None):
+    """Several independent products y_j = W_j x_j in one launch (see sage_gemv_multi)."""
     torch = _torch()
+    if len(xs) != len(ps):
+        raise ValueError("one input per matrix")
     if ys is None:
         ys = [torch.empty(p.d_out, dtype=torch.float16, device=x.device) for p, x in zip(ps, xs)]
-    if ws is None:
-        ws = workspace(gemv_multi_workspace_bytes(ps), xs[0].device)
+    for p, x, y in zip(ps, xs, ys):
+        _check_packed(p)
+        _require_vec("x", x, p.d_in)
+        _require_vec("y", y, p.d_out)
     arr = _mat_array(ps)
     xa = (ctypes.c_void_p * len(ps))(*[_ptr(x) for x in xs])
     ya = (ctypes.c_void_p * len(ps))(*[_ptr(y) for y in ys])
-    _check("sage_gemv_multi", lib().sage_gemv_multi(arr, xa, ya, len(ps), _ptr(ws), ws.numel(),
+    _check("sage_gemv_multi", lib().sage_gemv_multi(arr, xa, ya, len(ps), _ptr(ws),
+                                                    0 if ws is None else ws.numel(),
                                                     _stream(stream)))
     return ys
 
@@ -344,11 +391,20 @@ def gemm_small_workspace_bytes(p: Packed, M: int) -> int:
 
 
 def gemm_small(p: Packed, X, Y=None, ws=None, stream=None):
+    """Y = X W_hat^T for M activation rows (see sage_gemm_small)."""
     torch = _torch()
+    _check_packed(p)
     _require_cuda(X)
+    if X.dim() != 2 or str(X.dtype) != "torch.float16" or X.stride(1) != 1:
+        raise ValueError("X must be a 2-D float16 tensor with unit column stride")
     M = X.shape[0]
+    if X.shape[1] < p.d_in:
+        raise ValueError(f"X rows hold {X.shape[1]} values, need d_in = {p.d_in}")
     if Y is None:
         Y = torch.empty((M, p.d_out), dtype=torch.float16, device=X.device)
+    if (Y.dim() != 2 or str(Y.dtype) != "torch.float16" or Y.stride(1) != 1
+            or Y.shape[0] < M or Y.shape[1] < p.d_out):
+        raise ValueError("Y must be a float16 [M, >= d_out] tensor with unit column stride")
     if ws is None:
         ws = workspace(gemm_small_workspace_bytes(p, M), X.device)
     d = p.desc()
@@ -358,45 +414,84 @@ def gemm_small(p: Packed, X, Y=None, ws=None, stream=None):
     return Y
 
 
-def expert_table(experts: Sequence[Sequence[Packed]], device):
-    """Device array of descriptors, expert e's matrix j at e*n_mats + j (for moe_gemv).
+def expert_table(experts: Sequence, device):
+    """Device array of descriptors for moe_gemv / moe_gemv_grouped.
 
-    The returned tensor keeps references to the Packed matrices it points at, so their device
-    buffers stay allocated for as long as the table is alive."""
+    `experts` is a sequence of Packed (one matrix per expert) or of sequences of Packed (expert
+    e's matrix j at e*n_mats + j). The returned tensor keeps references to the Packed matrices it
+    points at, so their device buffers stay allocated for as long as the table is alive."""
     torch = _torch()
-    n_mats = len(experts[0])
-    flat = [m for ex in experts for m in ex]
+    if len(experts) == 0:
+        raise ValueError("no experts")
+    nested = not isinstance(experts[0], Packed)
+    n_mats = len(experts[0]) if nested else 1
+    flat = [m for ex in experts for m in ex] if nested else list(experts)
+    if nested and any(len(ex) != n_mats for ex in experts):
+        raise ValueError("every expert needs the same number of matrices")
+    for m in flat:
+        _check_packed(m)
     arr = _mat_array(flat)
     raw = bytes(arr)
     host = torch.frombuffer(bytearray(raw), dtype=torch.uint8)
     table = host.to(device)
     table._sage_matrices = flat
+    table._sage_n_mats = n_mats
     return table, n_mats
 
 
-def moe_gemv_workspace_bytes(shapes: Sequence[tuple], n_sel: int) -> int:
-    n = ctypes.c_size_t(0)
-    arr = (SageMatrix * len(shapes))(*[SageMatrix(o, i, 0, 0, None, None, None) for o, i in shapes])
-    _check("sage_moe_gemv_workspace_bytes",
-           lib().sage_moe_gemv_workspace_bytes(arr, len(shapes), n_sel, ctypes.byref(n)))
-    return n.value
+def _table_mats(table):
+    mats = getattr(table, "_sage_matrices", None)
+    if mats is None:
+        raise ValueError("use a table made by expert_table()")
+    return mats
 
 
-def moe_gemv(table, n_experts: int, shapes: Sequence[tuple], ids, xs, x_strides, ys, y_strides,
-             ws=None, stream=None):
-    """Grouped products over routed experts (see sage_moe_gemv in include/sage.h)."""
-    _require_cuda(table, ids)
-    n_mats = len(shapes)
-    if ws is None:
-        ws = workspace(moe_gemv_workspace_bytes(shapes, ids.numel()), ids.device)
-    sh = (SageMatrix * n_mats)(*[SageMatrix(o, i, 0, 0, None, None, None) for o, i in shapes])
+def _check_moe_slots(mats, n_mats, j, ids, x, x_stride, y, y_stride):
+    """Every expert's matrix j fits the slot strides and the x / y tensors for n_sel slots."""
+    n_sel = ids.numel()
+    d_in = max(mats[e * n_mats + j].d_in for e in range(len(mats) // n_mats))
+    d_out = max(mats[e * n_mats + j].d_out for e in range(len(mats) // n_mats))
+    if x_stride < 0 or x_stride % 2 or y_stride < 0:
+        raise ValueError("strides must be non-negative (x_stride even)")
+    if x_stride and x_stride < d_in:
+        raise ValueError("x_stride shorter than an expert's d_in")
+    if n_sel > 1 and y_stride < d_out:
+        raise ValueError("y_stride shorter than an expert's d_out")
+    _require_vec("x", x, (n_sel - 1) * x_stride + d_in)
+    _require_vec("y", y, (n_sel - 1) * y_stride + d_out)
+
+
+def moe_gemv(table, ids, x, x_stride: int, y, y_stride: int, stream=None):
+    """Batch-one products of the routed experts ids (int32 device tensor) in one launch: slot s
+    reads x[s*x_stride:] and writes y[s*y_stride:] (see sage_moe_gemv in include/sage.h)."""
+    mats = _table_mats(table)
+    if getattr(table, "_sage_n_mats", 1) != 1:
+        raise ValueError("moe_gemv takes a table with one matrix per expert")
+    _require_vec("ids", ids, 1, "int32")
+    _check_moe_slots(mats, 1, 0, ids, x, x_stride, y, y_stride)
+    _check("sage_moe_gemv", lib().sage_moe_gemv(
+        ctypes.cast(_ptr(table), _PM), len(mats), _ptr(ids), ids.numel(), _ptr(x), x_stride,
+        _ptr(y), y_stride, _stream(stream)))
+    return y
+
+
+def moe_gemv_grouped(table, ids, xs, x_strides, ys, y_strides, stream=None):
+    """moe_gemv over the n_mats matrices of every routed expert in one launch (see
+    sage_moe_gemv_grouped in include/sage.h)."""
+    mats = _table_mats(table)
+    n_mats = getattr(table, "_sage_n_mats", 1)
+    if not (len(xs) == len(ys) == len(x_strides) == len(y_strides) == n_mats):
+        raise ValueError("one x, y and stride pair per matrix of an expert")
+    _require_vec("ids", ids, 1, "int32")
+    for j in range(n_mats):
+        _check_moe_slots(mats, n_mats, j, ids, xs[j], x_strides[j], ys[j], y_strides[j])
     xa = (ctypes.c_void_p * n_mats)(*[_ptr(x) for x in xs])
     ya = (ctypes.c_void_p * n_mats)(*[_ptr(y) for y in ys])
     xsa = (ctypes.c_int64 * n_mats)(*x_strides)
     ysa = (ctypes.c_int64 * n_mats)(*y_strides)
-    _check("sage_moe_gemv", lib().sage_moe_gemv(
-        ctypes.cast(_ptr(table), _PM), n_experts, sh, n_mats, _ptr(ids), ids.numel(), xa, xsa,
-        ya, ysa, _ptr(ws), ws.numel(), _stream(stream)))
+    _check("sage_moe_gemv_grouped", lib().sage_moe_gemv_grouped(
+        ctypes.cast(_ptr(table), _PM), len(mats) // n_mats, n_mats, _ptr(ids), ids.numel(), xa,
+        xsa, ya, ysa, _stream(stream)))
     return ys
 
 
@@ -413,26 +508,3 @@ def stream_read(buf, nbytes: Optional[int] = None, sink=None, stream=None):
         sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
     _check("sage_stream_read", lib().sage_stream_read(_ptr(buf), n, _ptr(sink), _stream(stream)))
     return sink
-
-
-def mlp_workspace_bytes(gate: Packed, up: Packed, down: Packed) -> int:
-    n = ctypes.c_size_t(0)
-    g, u, d = gate.desc(), up.desc(), down.desc()
-    _check("sage_mlp_workspace_bytes", lib().sage_mlp_workspace_bytes(
-        ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), ctypes.byref(n)))
-    return n.value
-
-
-def mlp(gate: Packed, up: Packed, down: Packed, x, y=None, h=None, ws=None, stream=None):
-    """Fused SwiGLU block y = W_down (silu(W_gate x) * (W_up x)) (see sage_mlp in include/sage.h).
-    Pass h (fp16 [inter]) to also receive the intermediate vector."""
-    torch = _torch()
-    _require_cuda(x, y, h, ws)
-    if y is None:
-        y = torch.empty(down.d_out, dtype=torch.float16, device=x.device)
-    if ws is None:
-        ws = workspace(mlp_workspace_bytes(gate, up, down), x.device)
-    g, u, d = gate.desc(), up.desc(), down.desc()
-    _check("sage_mlp", lib().sage_mlp(ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), _ptr(x),
-                                      _ptr(y), _ptr(h), _ptr(ws), ws.numel(), _stream(stream)))
-    return y

@@ -55,7 +55,12 @@ const char* sage_status_string(int status) {
   }
 }
 
-int sage_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+int sage_version(void) { return 2 * 10000 + 0 * 100 + 0; }
+
+#ifndef SAGE_SOURCE_DIGEST
+#define SAGE_SOURCE_DIGEST "unknown"
+#endif
+const char* sage_source_digest(void) { return SAGE_SOURCE_DIGEST; }
 
 int sage_format_version(void) { return sage::kFormatVersion; }
 

@@ -23,12 +23,9 @@ __global__ void __launch_bounds__(256) dequant_kernel(const uint8_t* __restrict_
   const int j = sv % kSubPerGroup;
   const int lane = row % kTileRows;
   const uint8_t* b = packed + ((int64_t)(row / kTileRows) * ng + g) * kBlockBytes;
-  uint32_t p[8], grid;
-  const uint32_t x = read_lane_payload(b, lane, p, &grid);
-  const uint32_t sbyte = sign_of(p, x, j);
-  const uint32_t f = field_of(p, j);
-  const uint32_t z = f & ((1u << L) - 1u);
-  const uint32_t q = f >> L;
+  uint32_t p[8], x, grid, sbyte, z, q;
+  read_lane_block(b, lane, p, &x, &grid);
+  v3_fields(p, x, j, L, &sbyte, &z, &q);
   const double mu = (double)h2f(grid);
   const double delta = (double)h2f(grid >> 16);
   const double r = mu + (double)q * delta;

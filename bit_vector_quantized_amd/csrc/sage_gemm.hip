@@ -198,9 +198,14 @@ __global__ void __launch_bounds__(256) permute_gather_kernel(const uint16_t* __r
     Xp[(int64_t)m * d_in + p] = X[(int64_t)m * ldx + src];
 }
 
-__device__ inline uint32_t mul_pair(uint32_t c, half2_t r) {
-  const half2_t v = __builtin_bit_cast(half2_t, c) * r;
-  return __builtin_bit_cast(uint32_t, v);
+// fp16(r * c) for the two fp16 values of a dword: each weight is the fp32 product rounded once to
+// fp16, as the paper's prefill kernel decodes r_hat (s (.) c_z) in FP32 and then stores FP16 (App.
+// A.1).
+__device__ inline uint32_t scale_pair(uint32_t c, float r) {
+  const half2_t h = __builtin_bit_cast(half2_t, c);
+  const _Float16 lo = (_Float16)((float)h[0] * r);
+  const _Float16 hi = (_Float16)((float)h[1] * r);
+  return __builtin_bit_cast(uint32_t, half2_t{lo, hi});
 }
 
 // LDS layout: codebook replicas [K][16][16 B], 128 spare bytes, flag, then the X tile
@@ -348,26 +353,25 @@ __device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint
         // subvector 4u + kk of the group: payload dword 2u + kk/2, half a (kk even) or b (kk odd)
         const uint32_t P = (kk < 2) ? pp[k][0] : pp[k][1];
         const int pair = 2 * u + (kk >> 1);
-        uint32_t s, f;
+        uint32_t s, z, q;
         if ((kk & 1) == 0) {
-          s = ((P >> 4) & 15u) | ((P >> 28) << 4);
-          f = (P >> 8) & 1023u;
+          z = (P >> 3) & (kK - 1u);
+          q = (P >> (7 + L)) & ((1u << (10 - L)) - 1u);
+          s = ((P >> (3 + L)) & 15u) | (((sd[k][0] >> (4 * pair)) & 15u) << 4);
         } else {
-          s = (P & 15u) | (((sd[k][0] >> (4 * pair)) & 15u) << 4);
-          f = (P >> 18) & 1023u;
+          z = (P >> 17) & (kK - 1u);
+          q = (P >> (21 + L)) & ((1u << (10 - L)) - 1u);
+          s = ((P >> (17 + L)) & 15u) | ((P >> 31) << 4) | ((P & 7u) << 5);
         }
-        const uint32_t z = f & (kK - 1u);
-        const float r = fmaf((float)(f >> L), dl, mu);
-        const _Float16 rh = (_Float16)r;
-        const half2_t r2 = half2_t{rh, rh};
+        const float r = fmaf((float)q, dl, mu);
         const uint4 c = *reinterpret_cast<const uint4*>(cb + z * 256 + laneoff);
         const uint2 mlo = sign_masks(s & 15u);
         const uint2 mhi = sign_masks(s >> 4);
         uint32_t w[4];
-        w[0] = mul_pair(c.x ^ mlo.x, r2);
-        w[1] = mul_pair(c.y ^ mlo.y, r2);
-        w[2] = mul_pair(c.z ^ mhi.x, r2);
-        w[3] = mul_pair(c.w ^ mhi.y, r2);
+        w[0] = scale_pair(c.x ^ mlo.x, r);
+        w[1] = scale_pair(c.y ^ mlo.y, r);
+        w[2] = scale_pair(c.z ^ mhi.x, r);
+        w[3] = scale_pair(c.w ^ mhi.y, r);
         if (!row_ok) w[0] = w[1] = w[2] = w[3] = 0u;
         const half8_t b = __builtin_bit_cast(half8_t, make_uint4(w[0], w[1], w[2], w[3]));
         const int xcol = slot * kGroupCols + (4 * u + kk) * 8;
@@ -538,24 +542,24 @@ struct RowWords {
 struct Fetched {
   uint4 c;
   uint2 mlo, mhi;
-  half2_t r2;
+  float r;
 };
 
 template <int L>
 __device__ __forceinline__ Fetched decode_fetch(const RowWords& w, int s, int h, const uint8_t* cb,
                                                 uint32_t laneoff) {
   constexpr uint32_t kK = 1u << L;
+  constexpr uint32_t kV = (1u << (10 - L)) - 1u;
   const uint32_t P = s < 4 ? w.a[s & 3] : w.b[s & 3];
   const uint32_t X = w.side[0], G = w.side[1];
   // subvector 2s + h of the group: pair s, half a (h = 0) or b (h = 1)
-  const uint32_t f = (P >> (h ? 18 : 8)) & 1023u;
-  const uint32_t lo = h ? (P & 15u) : ((P >> 4) & 15u);
-  const uint32_t hi = h ? ((X >> (4 * s)) & 15u) : (P >> 28);
-  const float r = fmaf((float)(f >> L), h2f(G >> 16), h2f(G));
-  const _Float16 rh = (_Float16)r;
+  const uint32_t z = h ? ((P >> 17) & (kK - 1u)) : ((P >> 3) & (kK - 1u));
+  const uint32_t q = h ? ((P >> (21 + L)) & kV) : ((P >> (7 + L)) & kV);
+  const uint32_t lo = h ? ((P >> (17 + L)) & 15u) : ((P >> (3 + L)) & 15u);
+  const uint32_t hi = h ? ((P >> 31) | ((P & 7u) << 1)) : ((X >> (4 * s)) & 15u);
   Fetched o;
-  o.r2 = half2_t{rh, rh};
-  o.c = *reinterpret_cast<const uint4*>(cb + (f & (kK - 1u)) * 256 + laneoff);
+  o.r = fmaf((float)q, h2f(G >> 16), h2f(G));
+  o.c = *reinterpret_cast<const uint4*>(cb + z * 256 + laneoff);
   o.mlo = sign_masks(lo);
   o.mhi = sign_masks(hi);
   return o;
@@ -563,8 +567,8 @@ __device__ __forceinline__ Fetched decode_fetch(const RowWords& w, int s, int h,
 
 __device__ __forceinline__ half8_t decode_finish(const Fetched& d) {
   return __builtin_bit_cast(
-      half8_t, make_uint4(mul_pair(d.c.x ^ d.mlo.x, d.r2), mul_pair(d.c.y ^ d.mlo.y, d.r2),
-                          mul_pair(d.c.z ^ d.mhi.x, d.r2), mul_pair(d.c.w ^ d.mhi.y, d.r2)));
+      half8_t, make_uint4(scale_pair(d.c.x ^ d.mlo.x, d.r), scale_pair(d.c.y ^ d.mlo.y, d.r),
+                          scale_pair(d.c.z ^ d.mhi.x, d.r), scale_pair(d.c.w ^ d.mhi.y, d.r)));
 }
 
 template <int L, int kQ>

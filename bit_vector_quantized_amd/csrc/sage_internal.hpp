@@ -1,6 +1,6 @@
 // Internal definitions shared by the libsage translation units (not part of the C ABI).
 //
-// Packed layout (format version 2). Rows are grouped in tiles of 64 (one wavefront lane per row);
+// Packed layout (format version 3). Rows are grouped in tiles of 64 (one wavefront lane per row);
 // columns in groups of 128 (16 subvectors of 8 weights: the radius-grid group of the SAGE paper,
 // §3.1 / App. A.6). Each (row tile, column group) block is 2560 bytes and blocks are stored
 // row-tile major: block(rt, g) at byte (rt * n_groups + g) * 2560. Inside a block:
@@ -9,19 +9,23 @@
 //   bytes [1024, 2048)  plane B: lane l owns 16 bytes = payload dwords P4..P7
 //   bytes [2048, 2560)  side plane: lane l owns 8 bytes = dword X, then dword G = mu | delta << 16
 //
-// With s_j the sign byte of subvector j of the group (bit i <=> weight i negative), z_j its codeword
-// index, q_j its radius code and F_j = z_j | q_j << log2K (10 bits), payload dword P_i (i = 0..7)
-// carries the pair a = 2i, b = 2i + 1:
+// With L = log2(K), V = 10 - L, and for subvector j of the group its sign byte s_j (bit i <=>
+// weight i negative), codeword index z_j and radius code q_j, payload dword P_i (i = 0..7) carries
+// the pair a = 2i, b = 2i + 1:
 //
-//   bits [ 0, 4)  s_b & 15        bits [ 8,18)  F_a          bits [28,32)  s_a >> 4
-//   bits [ 4, 8)  s_a & 15        bits [18,28)  F_b
+//   bits [0, 3)        s_b bits 5..7          bits [17, 17+L)    z_b
+//   bits [3, 3+L)      z_a                    bits [17+L, 21+L)  s_b bits 0..3
+//   bits [3+L, 7+L)    s_a bits 0..3          bits [21+L, 31)    q_b
+//   bits [7+L, 17)     q_a                    bit  31            s_b bit 4
 //
-// and X carries s_{2i+1} >> 4 at bits [4i, 4i+4). Every subvector thus costs 8 + log2K + V = 18
-// bits (§3.1 Eq. (3)) and every group 4 more bytes of fp16 grid. The positions are chosen for the
-// decode kernel: each sign nibble sits in bits 4..7 of some byte (one masked select gives 16x the
-// nibble, a table offset), F_a sits at bit 8 (one and-or gives the codeword's LDS row and, with an
-// exponent OR-ed in, q as a float), F_b reaches the same position with one shift. Rows past d_out
-// in the last tile are zero.
+// and X carries s_{2i} bits 4..7 at bits [4i, 4i+4). Every subvector costs 8 + L + V = 18 bits
+// (§3.1 Eq. (3)) and every group 4 more bytes of fp16 grid: 2.5 bits per weight. The positions
+// serve the batch-one decoder, whose LDS table of sign-applied codeword halves is indexed by
+// (z | s_half << L) * 8 bytes: P & mask gives subvector a's first-half table address, the
+// rotation of P by 14 brings b's index, sign nibble and radius code to a's positions, rotating P
+// left by 4 + L brings b's second sign nibble (bits 31, 0, 1, 2) next to its index, and q sits at
+// bits [7+L, 17) of P or of the rotated P, where OR-ing an exponent turns it into the float
+// 2^(16-L) + q. Rows past d_out in the last tile are zero.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -32,7 +36,7 @@
 
 namespace sage {
 
-constexpr int kFormatVersion = 2;
+constexpr int kFormatVersion = 3;
 constexpr int kTileRows = 64;                  // rows per tile = lanes per wavefront
 constexpr int kGroupCols = 128;                // weights per radius-grid group
 constexpr int kSubPerGroup = 16;               // subvectors per group
@@ -41,30 +45,39 @@ constexpr int kPlaneA = 0;
 constexpr int kPlaneB = 1024;
 constexpr int kSidePlane = 2048;
 
-// Pack / unpack one subvector pair of a payload dword (format version 2).
-__host__ __device__ inline uint32_t pack_pair(uint32_t sa, uint32_t sb, uint32_t fa, uint32_t fb) {
-  return (sb & 15u) | ((sa & 15u) << 4) | ((fa & 1023u) << 8) | ((fb & 1023u) << 18) |
-         ((sa >> 4) << 28);
+// Payload dword of the pair (a, b) (format version 3). Field values must be in range.
+__host__ __device__ inline uint32_t v3_pair(uint32_t sa, uint32_t za, uint32_t qa, uint32_t sb,
+                                            uint32_t zb, uint32_t qb, int L) {
+  return (sb >> 5) | (za << 3) | ((sa & 15u) << (3 + L)) | (qa << (7 + L)) | (zb << 17) |
+         ((sb & 15u) << (17 + L)) | (qb << (21 + L)) | (((sb >> 4) & 1u) << 31);
 }
-// Reads the 8 payload dwords and X of (lane) in a block into p[0..7], returns X; G via *grid.
-__device__ inline uint32_t read_lane_payload(const uint8_t* blk, int lane, uint32_t p[8],
-                                             uint32_t* grid) {
+
+// Fields of subvector j (0..15) of a group from its payload dwords P[0..7] and X.
+__host__ __device__ inline void v3_fields(const uint32_t P[8], uint32_t X, int j, int L,
+                                          uint32_t* s, uint32_t* z, uint32_t* q) {
+  const uint32_t w = P[j >> 1];
+  const uint32_t kmask = (1u << L) - 1u, vmask = (1u << (10 - L)) - 1u;
+  if ((j & 1) == 0) {
+    *z = (w >> 3) & kmask;
+    *q = (w >> (7 + L)) & vmask;
+    *s = ((w >> (3 + L)) & 15u) | (((X >> (4 * (j >> 1))) & 15u) << 4);
+  } else {
+    *z = (w >> 17) & kmask;
+    *q = (w >> (21 + L)) & vmask;
+    *s = ((w >> (17 + L)) & 15u) | ((w >> 31) << 4) | ((w & 7u) << 5);
+  }
+}
+
+// The 8 payload dwords, X and G of one lane of a block.
+__device__ inline void read_lane_block(const uint8_t* blk, int lane, uint32_t p[8], uint32_t* x,
+                                       uint32_t* grid) {
   const uint4 a = *reinterpret_cast<const uint4*>(blk + kPlaneA + lane * 16);
   const uint4 b = *reinterpret_cast<const uint4*>(blk + kPlaneB + lane * 16);
   const uint2 s = *reinterpret_cast<const uint2*>(blk + kSidePlane + lane * 8);
   p[0] = a.x; p[1] = a.y; p[2] = a.z; p[3] = a.w;
   p[4] = b.x; p[5] = b.y; p[6] = b.z; p[7] = b.w;
+  *x = s.x;
   *grid = s.y;
-  return s.x;
-}
-// Sign byte, and 10-bit index/radius field of subvector j (0..15) from the payload and X.
-__device__ inline uint32_t sign_of(const uint32_t p[8], uint32_t x, int j) {
-  const uint32_t w = p[j >> 1];
-  return (j & 1) ? ((w & 15u) | (((x >> (4 * (j >> 1))) & 15u) << 4))
-                 : (((w >> 4) & 15u) | ((w >> 28) << 4));
-}
-__device__ inline uint32_t field_of(const uint32_t p[8], int j) {
-  return (p[j >> 1] >> ((j & 1) ? 18 : 8)) & 1023u;
 }
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -90,6 +103,13 @@ inline size_t packed_bytes(int d_out, int d_in) {
 int check_matrix(const sage_matrix_t* m);   // shape, split, pointers, alignment
 int hip_status();                            // SAGE_ERR_HIP if the last launch failed
 int device_cu_count();                       // compute units of the current device (cached)
+
+// Range-checked buffer view: loads at offsets past `bytes` return zeros without a memory access.
+__device__ inline __amdgpu_buffer_rsrc_t view(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+constexpr uint32_t kNowhere = 1u << 30;  // an offset past every range
+constexpr int kNonTemporal = 2;          // streamed once: no reuse expected in the caches
 
 // Global-memory view of a device pointer. Pointers read from memory (descriptor tables) are
 // generic, and loads through them compile to flat instructions, which count against both the

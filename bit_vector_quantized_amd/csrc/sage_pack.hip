@@ -1,6 +1,6 @@
 // sage_pack / sage_unpack: move the separate code fields of a matrix (SAGE paper §3.1: sign bits,
 // codeword index, radius code, and the fp16 grid of every 128-weight group) into and out of the
-// packed streaming layout described in sage_internal.hpp.
+// packed streaming layout (format version 3) described in sage_internal.hpp.
 #include "sage_internal.hpp"
 
 namespace sage {
@@ -37,15 +37,17 @@ __global__ void __launch_bounds__(256) pack_kernel(const uint8_t* __restrict__ s
     const uint32_t qw[4] = {qi.x, qi.y, qi.z, qi.w};
     const uint32_t kmask = (1u << L) - 1u;
     const uint32_t vmask = (1u << (10 - L)) - 1u;
-    uint32_t sj[kSubPerGroup], fj[kSubPerGroup];
+    uint32_t sj[kSubPerGroup], zj[kSubPerGroup], qj[kSubPerGroup];
     for (int j = 0; j < kSubPerGroup; ++j) {
       const int sh = 8 * (j & 3);
       sj[j] = (sw[j >> 2] >> sh) & 0xFFu;
-      fj[j] = ((zw[j >> 2] >> sh) & kmask) | (((qw[j >> 2] >> sh) & vmask) << L);
+      zj[j] = (zw[j >> 2] >> sh) & kmask;
+      qj[j] = (qw[j >> 2] >> sh) & vmask;
     }
     for (int i = 0; i < 8; ++i) {
-      p[i] = pack_pair(sj[2 * i], sj[2 * i + 1], fj[2 * i], fj[2 * i + 1]);
-      x |= (sj[2 * i + 1] >> 4) << (4 * i);
+      const int a = 2 * i, bb = 2 * i + 1;
+      p[i] = v3_pair(sj[a], zj[a], qj[a], sj[bb], zj[bb], qj[bb], L);
+      x |= (sj[a] >> 4) << (4 * i);
     }
     const size_t go = (size_t)row * ng + g;
     grid = (uint32_t)mu[go] | ((uint32_t)delta[go] << 16);
@@ -72,16 +74,16 @@ __global__ void __launch_bounds__(256) unpack_kernel(const uint8_t* __restrict__
   const int row = (int)(blk / ng) * kTileRows + lane;
   if (row >= d_out) return;
   const uint8_t* b = packed + blk * kBlockBytes;
-  uint32_t p[8], grid;
-  const uint32_t x = read_lane_payload(b, lane, p, &grid);
+  uint32_t p[8], x, grid;
+  read_lane_block(b, lane, p, &x, &grid);
   uint32_t so[4] = {0, 0, 0, 0}, zo[4] = {0, 0, 0, 0}, qo[4] = {0, 0, 0, 0};
-  const uint32_t kmask = (1u << L) - 1u;
   for (int j = 0; j < kSubPerGroup; ++j) {
     const int sh = 8 * (j & 3);
-    const uint32_t f = field_of(p, j);
-    so[j >> 2] |= sign_of(p, x, j) << sh;
-    zo[j >> 2] |= (f & kmask) << sh;
-    qo[j >> 2] |= (f >> L) << sh;
+    uint32_t sv, zv, qv;
+    v3_fields(p, x, j, L, &sv, &zv, &qv);
+    so[j >> 2] |= sv << sh;
+    zo[j >> 2] |= zv << sh;
+    qo[j >> 2] |= qv << sh;
   }
   const size_t off = (size_t)row * m + (size_t)g * kSubPerGroup;
   *reinterpret_cast<uint4*>(signs + off) = make_uint4(so[0], so[1], so[2], so[3]);

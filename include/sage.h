@@ -61,6 +61,10 @@ const char* sage_status_string(int status);
 int sage_version(void);
 int sage_format_version(void);
 
+/* sha256 prefix (16 hex digits) of the library's sources as built (static storage), so a result
+ * can name the exact sources it was measured on. */
+const char* sage_source_digest(void);
+
 /*
  * A quantised matrix as the decode kernels read it.
  *   d_out, d_in  weight shape (rows are outputs); d_in is a multiple of 128.
@@ -114,23 +118,24 @@ int sage_dequant(const sage_matrix_t* m, uint16_t* w, sage_stream_t stream);
 
 /*
  * sage_gemv: y = W_hat x for one input vector (batch one), the decode step of §3.5 / App. A.1.
- *   x   fp16 [d_in], original channel order (the kernel gathers it through pi), 4-byte aligned.
+ *   x   fp16 [d_in], 4-byte aligned: original channel order (gathered through pi inside the
+ *       call, §3.5 eager decoding), or stored order when the descriptor's pi is NULL (the input's
+ *       producer applied the permutation, §3.5 compiled decoding).
  *   y   fp16 [d_out], 2-byte aligned; written, not accumulated.
- *   ws  workspace of at least sage_gemv_workspace_bytes() bytes, 256-byte aligned. It must be
- *       zero-filled before its first use; every call leaves it ready for the next call (its
- *       counters return to zero). A workspace must not be shared by calls that can overlap.
- *       May be NULL when the required size is 0.
- * Accumulation is fp32; the result is rounded once to fp16.
+ *   ws  unused (the product needs no workspace; sage_gemv_workspace_bytes() reports 0); may be
+ *       NULL.
+ * d_in is at most 32768 (16384 when pi is not NULL); larger inputs return SAGE_ERR_SHAPE.
+ * Accumulation is fp32; the result is rounded once to fp16. Repeated calls give the same bits.
  */
 int sage_gemv_workspace_bytes(const sage_matrix_t* m, size_t* bytes);
 int sage_gemv(const sage_matrix_t* m, const uint16_t* x, uint16_t* y, void* ws, size_t ws_bytes,
               sage_stream_t stream);
 
 /*
- * sage_gemv_multi: several independent products y_j = W_j x_j in one launch (for example the
+ * sage_gemv_multi: up to 16 independent products y_j = W_j x_j in one launch (for example the
  * q/k/v or gate/up projections that read the same input). mats, xs and ys are HOST arrays of
- * n entries; the pointers inside are device pointers with the alignments of sage_gemv. The
- * workspace requirement is sage_gemv_multi_workspace_bytes() for the same list.
+ * n entries; the pointers inside are device pointers with the alignments of sage_gemv. No
+ * workspace is used (the *_workspace_bytes query reports 0; ws may be NULL).
  */
 int sage_gemv_multi_workspace_bytes(const sage_matrix_t* mats, int n, size_t* bytes);
 int sage_gemv_multi(const sage_matrix_t* mats, const uint16_t* const* xs, uint16_t* const* ys,
@@ -149,63 +154,44 @@ int sage_gemv_multi(const sage_matrix_t* mats, const uint16_t* const* xs, uint16
  *       holds X in permuted column order (written by the call) and the split partial sums.
  *       When the matrix has pi = NULL (X already in stored column order, e.g. written permuted
  *       by its producer) and X is 16-byte aligned with ldx a multiple of 8, X is read in place
- *       and no reorder runs.
+ *       and no reorder runs. The workspace must be zero-filled before its first use; every call
+ *       leaves it ready for the next. Calls that share a workspace must not overlap.
  */
 int sage_gemm_small_workspace_bytes(const sage_matrix_t* m, int M, size_t* bytes);
 int sage_gemm_small(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, uint16_t* Y,
                     int ldy, void* ws, size_t ws_bytes, sage_stream_t stream);
 
 /*
- * sage_moe_gemv: grouped batch-one products over routed experts in one launch.
- *   experts_dev  DEVICE array [n_experts * n_mats] of sage_matrix_t, 8-byte aligned; expert e's
- *                matrix j is entry e*n_mats + j. Splits, codebooks, permutations and packed
- *                buffers may differ per expert; the shape of matrix j must equal shapes[j] for
- *                every expert (the device copy's d_out/d_in are not read).
- *   shapes       HOST array [n_mats]; only d_out and d_in of each entry are used.
+ * sage_moe_gemv: batch-one products of the routed experts of a mixture-of-experts layer in one
+ * launch. The paper evaluates mixture-of-experts models (Qwen3-30B-A3B) but describes no expert
+ * kernel; this is the batch-one product above applied to each routed expert's own matrix.
+ *   experts_dev  DEVICE array [n_experts] of sage_matrix_t (8-byte aligned): expert e's matrix,
+ *                with its own shape, split, codebook, pi and packed buffer (all read on the
+ *                device). d_in at most 32768 (16384 with a pi).
  *   ids_dev      DEVICE int32 [n_sel], 4-byte aligned: the routed experts, each in [0, n_experts).
- *   xs, ys       HOST arrays [n_mats] of DEVICE fp16 pointers. Slot s of matrix j reads
- *                xs[j] + s*x_strides[j] (a stride of 0 shares one input, e.g. the token for
- *                gate/up) and writes ys[j] + s*y_strides[j] (d_out[j] values).
- *   x_strides, y_strides  HOST int64 [n_mats], in elements; x strides even, y strides >= d_out
- *                when n_sel > 1.
- *   ws           workspace of sage_moe_gemv_workspace_bytes() bytes, zero-filled before first use
- *                (kept zero-ready across calls, as for sage_gemv).
- * One launch covers a mixture-of-experts layer's routed matrices (gate/up on the shared token,
- * down on each expert's own intermediate vector); the router's combine stays with the caller.
+ *   x, x_stride  slot s reads x + s*x_stride (x_stride in elements, even; 0 = one input shared by
+ *                every slot, e.g. the token for the gate/up projections). 4-byte aligned.
+ *   y, y_stride  slot s writes y + s*y_stride (d_out of its expert values); y_stride >= every
+ *                selected expert's d_out when n_sel > 1. 2-byte aligned.
+ * A slot whose id is out of range, or whose descriptor has an invalid shape or split, is skipped:
+ * its output is not written. The router's weighted combine stays with the caller. No workspace.
+ * Errors: SAGE_ERR_NULL, SAGE_ERR_ALIGN, SAGE_ERR_ARG (n_experts, n_sel < 1, bad strides),
+ * SAGE_ERR_HIP.
  */
-int sage_moe_gemv_workspace_bytes(const sage_matrix_t* shapes, int n_mats, int n_sel,
-                                  size_t* bytes);
-int sage_moe_gemv(const sage_matrix_t* experts_dev, int n_experts, const sage_matrix_t* shapes,
-                  int n_mats, const int32_t* ids_dev, int n_sel, const uint16_t* const* xs,
-                  const int64_t* x_strides, uint16_t* const* ys, const int64_t* y_strides,
-                  void* ws, size_t ws_bytes, sage_stream_t stream);
+int sage_moe_gemv(const sage_matrix_t* experts_dev, int n_experts, const int32_t* ids_dev,
+                  int n_sel, const uint16_t* x, int64_t x_stride, uint16_t* y, int64_t y_stride,
+                  sage_stream_t stream);
 
-/* ------------------------------------------------------------------------------------------
- * sage_mlp: the SwiGLU feed-forward block of a decoder layer at batch one in one launch,
- *   y = W_down (silu(W_gate x) * (W_up x)),  silu(t) = t / (1 + exp(-t)),
- * with W_gate, W_up [inter x hidden] and W_down [hidden_out x inter] SAGE-packed (any splits).
- * The intermediate follows the unfused sequence of fp16 tensors: gate and up rows are rounded to
- * fp16, silu and the product are computed in fp32 from those values and rounded to fp16, and that
- * vector is the input of W_down (gathered through W_down's pi like any other input). The
- * down-projection workgroups are dispatched after the gate/up ones, issue their weight loads,
- * then wait (bounded) until every gate/up row group has been written.
- *   gate, up, down  matrices as for sage_gemv; gate/up same shape, down->d_in == gate->d_out;
- *                   hidden and inter at most 16384.
- *   x   fp16 [hidden], original channel order of W_gate/W_up, 16-byte aligned.
- *   y   fp16 [down->d_out], 2-byte aligned.
- *   h   optional fp16 [inter] copy of the intermediate (NULL: not written), 8-byte aligned.
- *   ws  workspace of sage_mlp_workspace_bytes() bytes, 256-byte aligned, zero-filled before its
- *       first use and left zero-ready by every call (as for sage_gemv). A wait that ran out, which
- *       needs the down-projection workgroups to be starved for ~0.1 s, is counted in a word of
- *       ws; results of such a call are undefined and ws must be zero-filled again.
- * Calls that share a workspace must not overlap. Errors: SAGE_ERR_NULL, _SHAPE (shapes that do
- * not chain, or wider than 16384), _SPLIT, _ALIGN, _WORKSPACE, _HIP.
+/*
+ * sage_moe_gemv_grouped: sage_moe_gemv over n_mats (1..4) matrices per expert in one launch, for
+ * example an expert's gate and up projections on the shared token. experts_dev holds
+ * [n_experts * n_mats] descriptors, expert e's matrix j at e*n_mats + j; xs, ys, x_strides and
+ * y_strides are HOST arrays [n_mats] giving matrix j's input and output as x and y above.
  */
-int sage_mlp_workspace_bytes(const sage_matrix_t* gate, const sage_matrix_t* up,
-                             const sage_matrix_t* down, size_t* bytes);
-int sage_mlp(const sage_matrix_t* gate, const sage_matrix_t* up, const sage_matrix_t* down,
-             const uint16_t* x, uint16_t* y, uint16_t* h, void* ws, size_t ws_bytes,
-             sage_stream_t stream);
+int sage_moe_gemv_grouped(const sage_matrix_t* experts_dev, int n_experts, int n_mats,
+                          const int32_t* ids_dev, int n_sel, const uint16_t* const* xs,
+                          const int64_t* x_strides, uint16_t* const* ys, const int64_t* y_strides,
+                          sage_stream_t stream);
 
 /* ------------------------------------------------------------------------------------------
  * sage_stream_read: measurement helper, not part of the decode path. Reads `bytes` bytes at `p`

@@ -21,7 +21,8 @@ def test_exports_every_declared_function(L):
     assert len(names) >= 15
     for n in names:
         assert hasattr(L, n), n
-    assert L.sage_format_version() >= 1 and L.sage_version() >= 10000
+    assert L.sage_format_version() == 3 and L.sage_version() >= 20000
+    assert len(sage.source_digest()) == 16
 
 
 def test_status_strings(L):
@@ -73,13 +74,14 @@ def test_gemv_validation(L):
     assert L.sage_gemv(ctypes.byref(_desc(codebook=8194)), x, y, None, 0, None) == ALIGN
     assert L.sage_gemv(ctypes.byref(_desc()), None, y, None, 0, None) == NULL
     assert L.sage_gemv(ctypes.byref(_desc()), ctypes.c_void_p((1 << 20) + 2), y, None, 0, None) == ALIGN
-    # a large matrix needs split-K partials: without a workspace the call is refused
+    # the product needs no workspace
+    n = ctypes.c_size_t(7)
     big = _desc(d_out=2560, d_in=9728)
-    n = ctypes.c_size_t(0)
-    assert L.sage_gemv_workspace_bytes(ctypes.byref(big), ctypes.byref(n)) == OK
-    assert n.value > 0
-    assert L.sage_gemv(ctypes.byref(big), x, y, None, 0, None) == WS
-    assert L.sage_gemv(ctypes.byref(big), x, y, ctypes.c_void_p(1 << 24), n.value - 1, None) == WS
+    assert L.sage_gemv_workspace_bytes(ctypes.byref(big), ctypes.byref(n)) == OK and n.value == 0
+    # inputs wider than the workgroup stages in LDS are refused before any launch
+    assert L.sage_gemv(ctypes.byref(_desc(d_in=33792)), x, y, None, 0, None) == SHAPE
+    assert L.sage_gemv(ctypes.byref(_desc(d_in=12288, log2K=8, V=2, pi=1 << 23)), x, y, None, 0,
+                       None) == SHAPE
 
 
 def test_gemm_and_multi_validation(L):
@@ -99,22 +101,31 @@ def test_gemm_and_multi_validation(L):
 
 
 def test_moe_validation(L):
-    shapes = (SageMatrix * 3)(_desc(d_out=768, d_in=2048), _desc(d_out=768, d_in=2048),
-                              _desc(d_out=2048, d_in=768))
-    xs = (ctypes.c_void_p * 3)(1 << 20, 1 << 20, 1 << 22)
-    ys = (ctypes.c_void_p * 3)(1 << 23, 1 << 24, 1 << 25)
-    xst = (ctypes.c_int64 * 3)(0, 0, 768)
-    yst = (ctypes.c_int64 * 3)(768, 768, 2048)
     tab = ctypes.cast(ctypes.c_void_p(1 << 26), ctypes.POINTER(SageMatrix))
     ids = ctypes.c_void_p(1 << 27)
-    assert L.sage_moe_gemv(tab, 128, shapes, 3, ids, 0, xs, xst, ys, yst, None, 0, None) == ARG
-    assert L.sage_moe_gemv(tab, 4, shapes, 3, ids, 8, xs, xst, ys, yst, None, 0, None) == ARG
-    bad = (ctypes.c_int64 * 3)(0, 0, 767)
-    assert L.sage_moe_gemv(tab, 128, shapes, 3, ids, 8, xs, bad, ys, yst, None, 0, None) == ARG
-    small_y = (ctypes.c_int64 * 3)(100, 768, 2048)
-    assert L.sage_moe_gemv(tab, 128, shapes, 3, ids, 8, xs, xst, ys, small_y, None, 0, None) == ARG
-    n = ctypes.c_size_t(0)
-    assert L.sage_moe_gemv_workspace_bytes(shapes, 3, 8, ctypes.byref(n)) == OK
+    x = ctypes.c_void_p(1 << 20)
+    y = ctypes.c_void_p(1 << 21)
+    assert L.sage_moe_gemv(None, 128, ids, 8, x, 0, y, 2048, None) == NULL
+    assert L.sage_moe_gemv(tab, 128, None, 8, x, 0, y, 2048, None) == NULL
+    assert L.sage_moe_gemv(tab, 128, ids, 8, None, 0, y, 2048, None) == NULL
+    assert L.sage_moe_gemv(tab, 0, ids, 8, x, 0, y, 2048, None) == ARG
+    assert L.sage_moe_gemv(tab, 128, ids, 0, x, 0, y, 2048, None) == ARG
+    assert L.sage_moe_gemv(tab, 128, ids, 8, x, 767, y, 2048, None) == ARG
+    assert L.sage_moe_gemv(tab, 128, ids, 8, x, -2, y, 2048, None) == ARG
+    assert L.sage_moe_gemv(tab, 128, ids, 8, x, 0, y, 0, None) == ARG
+    assert L.sage_moe_gemv(ctypes.cast(ctypes.c_void_p((1 << 26) + 4), ctypes.POINTER(SageMatrix)),
+                           128, ids, 8, x, 0, y, 2048, None) == ALIGN
+    assert L.sage_moe_gemv(tab, 128, ctypes.c_void_p((1 << 27) + 2), 8, x, 0, y, 2048, None) == ALIGN
+    assert L.sage_moe_gemv(tab, 128, ids, 8, ctypes.c_void_p((1 << 20) + 2), 0, y, 2048, None) == ALIGN
+    xs = (ctypes.c_void_p * 2)(1 << 20, 1 << 20)
+    ys = (ctypes.c_void_p * 2)(1 << 21, 1 << 22)
+    st = (ctypes.c_int64 * 2)(0, 0)
+    yst = (ctypes.c_int64 * 2)(768, 768)
+    assert L.sage_moe_gemv_grouped(tab, 128, 0, ids, 8, xs, st, ys, yst, None) == ARG
+    assert L.sage_moe_gemv_grouped(tab, 128, 5, ids, 8, xs, st, ys, yst, None) == ARG
+    assert L.sage_moe_gemv_grouped(tab, 128, 2, ids, 8, xs, None, ys, yst, None) == NULL
+    bad = (ctypes.c_void_p * 2)(1 << 20, None)
+    assert L.sage_moe_gemv_grouped(tab, 128, 2, ids, 8, bad, st, ys, yst, None) == NULL
 
 
 def test_stream_read_validation(L):
@@ -166,3 +177,85 @@ def test_producer_validation(L):
     assert L.sage_silu_mul_permute(a, None, 1, 128, 128, None, a, 128, None) == NULL
     assert L.sage_silu_mul_permute(a, a, 70000, 128, 128, None, a, 128, None) == SHAPE
     assert L.sage_silu_mul_permute(a, a, 1, 128, 128, None, ctypes.c_void_p(4097), 128, None) == ALIGN
+
+
+# ------------------------------------------------------------------------------------------------
+# The binding's own checks (argument marshalling only, no device work). Stand-in tensors expose the
+# attributes the checks read, so these run without a GPU.
+# ------------------------------------------------------------------------------------------------
+
+class _FakeT:
+    def __init__(self, n, dtype="float16", cuda=True, contiguous=True, ptr=1 << 20, esize=2):
+        import torch
+        self._n, self.dtype, self.is_cuda = n, getattr(torch, dtype), cuda
+        self._c, self._p, self._e = contiguous, ptr, esize
+
+    def numel(self):
+        return self._n
+
+    def is_contiguous(self):
+        return self._c
+
+    def data_ptr(self):
+        return self._p
+
+    def element_size(self):
+        return self._e
+
+
+def _fake_packed(d_out=64, d_in=256, log2K=6, V=4, cb=None, pi="ok", packed_bytes=None):
+    nbytes = sage.packed_bytes(d_out, d_in, log2K, V) if packed_bytes is None else packed_bytes
+    return sage.Packed(d_out, d_in, log2K, V, _FakeT(nbytes, "uint8", esize=1),
+                       _FakeT(8 << log2K) if cb is None else cb,
+                       _FakeT(d_in, "int32", esize=4) if pi == "ok" else pi)
+
+
+def test_binding_rejects_wrong_vectors():
+    p = _fake_packed()
+    with pytest.raises(ValueError, match="at least 256"):
+        sage.gemv(p, _FakeT(255))
+    with pytest.raises(ValueError, match="float16"):
+        sage.gemv(p, _FakeT(256, "float32"))
+    with pytest.raises(ValueError, match="contiguous"):
+        sage.gemv(p, _FakeT(256, contiguous=False))
+    with pytest.raises(ValueError, match="device"):
+        sage.gemv(p, _FakeT(256, cuda=False))
+    with pytest.raises(ValueError, match="y has"):
+        sage.gemv(p, _FakeT(256), y=_FakeT(63))
+
+
+def test_binding_rejects_mismatched_matrix_buffers():
+    with pytest.raises(ValueError, match="codebook"):
+        sage.gemv(_fake_packed(cb=_FakeT(8 * 32)), _FakeT(256))
+    with pytest.raises(ValueError, match="pi"):
+        sage.gemv(_fake_packed(pi=_FakeT(255, "int32", esize=4)), _FakeT(256))
+    with pytest.raises(ValueError, match="packed"):
+        sage.gemv(_fake_packed(packed_bytes=100), _FakeT(256))
+    with pytest.raises(ValueError, match="out has"):
+        sage.dequant(_fake_packed(), out=_FakeT(64 * 256 - 1))
+
+
+def test_expert_table_keeps_its_matrices_alive():
+    """The device descriptor table holds references to the matrices it points at: dropping the
+    caller's list must not free them while the table lives (the cause of a past GPU fault)."""
+    import gc
+    import weakref
+    mats = [_fake_packed() for _ in range(3)]
+    table, n_mats = sage.expert_table(mats, "cpu")
+    assert n_mats == 1
+    refs = [weakref.ref(m) for m in mats]
+    del mats
+    gc.collect()
+    assert all(r() is not None for r in refs)
+    assert [m.packed.data_ptr() for m in table._sage_matrices] == [1 << 20] * 3
+    del table
+    gc.collect()
+    assert all(r() is None for r in refs)
+
+
+def test_expert_table_grouped_layout():
+    mats = [[_fake_packed(), _fake_packed(d_out=128)] for _ in range(2)]
+    table, n_mats = sage.expert_table(mats, "cpu")
+    assert n_mats == 2 and table.numel() == 4 * ctypes.sizeof(SageMatrix)
+    with pytest.raises(ValueError, match="same number"):
+        sage.expert_table([[_fake_packed()], [_fake_packed(), _fake_packed()]], "cpu")
