@@ -4,11 +4,11 @@
 // Work decomposition. Rows are taken in chunks of 16 (a quarter of a packed row tile). A workgroup
 // of 1024 threads (16 wavefronts, one workgroup per compute unit) owns whole rows: a run of chunks
 // of one product, so no partial sum ever leaves the compute unit (no split-K hand-off between
-// workgroups). Its 64 lane groups of 16 lanes split the workgroup's (chunk, half-group) units into
-// contiguous, equally long ranges in chunk-major order; lane l of a group owns row l of the chunk
-// it is working on. A range crosses at most one chunk boundary, so a lane keeps two sums. At the
-// end the lane groups that worked on a chunk add their sums in LDS in lane-group order (a fixed
-// order: results are reproducible bit for bit) and one rounding to fp16 gives y.
+// workgroups). Its (chunk, half-group) units, chunk-major, are cut into 64 contiguous ranges whose
+// lengths differ by at most one, one per lane group of 16 lanes; lane l of a group owns row l of
+// the chunk it is working on. A range crosses at most one chunk boundary, so a lane keeps two sums.
+// At the end one thread per row adds the sums of the ranges covering its chunk in range order (a
+// fixed order: results are reproducible bit for bit) and one rounding to fp16 gives y.
 //
 // Decode. The workgroup builds, once, a table of sign-applied codeword halves in LDS:
 // T[h][s][z] (h = first or second half of the 8-wide codeword, s = 4 sign bits, z = codeword) holds
@@ -108,17 +108,6 @@ __device__ inline void lds_store16(uint32_t addr, u32x4 v) {
   *(__attribute__((address_space(3))) u32x4*)(size_t)addr = v;
 }
 
-// First step of a dot chain, accumulator 0 (the VOP3P form takes the constant; the accumulating
-// VOP2 form would need a register zeroed first).
-__device__ inline float dot2_z(uint32_t a, uint32_t b) {
-  float r;
-  asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
-__device__ inline float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
-                                false);
-}
 __device__ inline uint32_t rotr(uint32_t v, uint32_t n) { return __builtin_amdgcn_alignbit(v, v, n); }
 // (a & m) | c as one v_and_or_b32 with m in a scalar register.
 __device__ inline uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
@@ -151,42 +140,72 @@ struct Unit {
   u32x2 s;  // X, G
 };
 
-// Per lane-group work: units [u0, u0 + cnt) of the workgroup, chunk-major; the first kb of them
-// lie in the lane group's first chunk cf (at half-groups hf, hf + 1, ...), the rest in chunk cf + 1.
+// floor(n / d) for 0 <= n < 2^16, given r = v_rcp_f32(d) for an integer 1 <= d < 2^16: n + 1/2 over
+// d lies at least 1/(2d) from every integer, and the float product's error is below (n/d) 2^-21.
+__device__ inline int div_small(int n, float r) { return (int)(((float)n + 0.5f) * r); }
+
+// Per lane-group work. A workgroup's units (chunk, half-group), chunk-major, are split into 64
+// contiguous ranges, range w for lane group w (so a wavefront's four ranges are neighbours and
+// differ in length only where the longer ranges end). Range w is units [u0, u0 + cnt); its first
+// kb units lie in chunk cf (half-groups hf, hf + 1, ...), the rest in chunk cf + 1.
 struct LaneWork {
-  int cnt, cf, hf, kb;
+  int u0, cnt, cf, hf, kb;
 };
 
-__device__ inline LaneWork lane_work(int lg, int nc, int nh) {
-  const int U = nc * nh;
-  const int base = U >> 6, rem = U & 63;
-  LaneWork w;
-  w.cnt = base + (lg < rem ? 1 : 0);
-  const int u0 = lg * base + min(lg, rem);
-  w.cf = u0 / nh;
-  w.hf = u0 - w.cf * nh;
-  w.kb = nh - w.hf;
-  return w;
+__device__ inline LaneWork lane_work(int w, int nu, int nh, float rcp_nh) {
+  const int base = nu >> 6, rem = nu & 63;
+  LaneWork r;
+  r.cnt = base + (w < rem ? 1 : 0);
+  r.u0 = w * base + min(w, rem);
+  r.cf = div_small(r.u0, rcp_nh);
+  r.hf = r.u0 - r.cf * nh;
+  r.kb = nh - r.hf;
+  return r;
 }
-// Lane group holding unit u (inverse of the split above).
-__device__ inline int lane_group_of(int u, int base, int rem) {
+// Range holding unit u (inverse of the split above).
+__device__ inline int range_of(int u, int base, int rem) {
   if (base == 0) return u;
   const int big = (base + 1) * rem;
-  return u < big ? u / (base + 1) : rem + (u - big) / base;
+  return u < big ? div_small(u, __builtin_amdgcn_rcpf((float)(base + 1)))
+                 : rem + div_small(u - big, __builtin_amdgcn_rcpf((float)base));
 }
 
-// Decode the 8 subvectors of one half-group unit and add them to acc.
+// Dot product of one subvector's 8 sign-applied codeword values (lo, hi: four fp16 pairs) with its
+// 8 inputs, which lanes 2j and 2j + 1 of the lane group hold (two fp16 pairs each). The lane group
+// is a DPP row of 16 lanes, and row_newbcast hands every lane of the row the given lane's register
+// as the dot's first operand: no LDS traffic for the input. The leading s_nop gives the two wait
+// states a DPP read needs after a VALU write of its source (the inputs come from an LDS read, but
+// the block does not rely on that).
+template <int J>
+__device__ __forceinline__ float dot8_row(u32x2 lo, u32x2 hi, uint32_t x0, uint32_t x1) {
+  float t;
+  asm("s_nop 1\n\t"
+      "v_mov_b32 %0, 0\n\t"
+      "v_dot2c_f32_f16_dpp %0, %5, %1 row_newbcast:%7 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_f16_dpp %0, %6, %2 row_newbcast:%7 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_f16_dpp %0, %5, %3 row_newbcast:%8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_f16_dpp %0, %6, %4 row_newbcast:%8 row_mask:0xf bank_mask:0xf"
+      : "=&v"(t)
+      : "v"(lo[0]), "v"(lo[1]), "v"(hi[0]), "v"(hi[1]), "v"(x0), "v"(x1), "n"(2 * J),
+        "n"(2 * J + 1));
+  return t;
+}
+
+// Decode the 8 subvectors of one half-group unit and add them to acc. xa: LDS address of the
+// unit's 64 inputs; lane l of the lane group reads inputs 4l .. 4l + 3.
 template <int L>
-__device__ __forceinline__ float decode_unit(const Unit& U, uint32_t half, uint32_t xa, float acc) {
+__device__ __forceinline__ float decode_unit(const Unit& U, uint32_t half, uint32_t xa, int l16,
+                                             float acc) {
   using S = Split<L>;
+  const u32x2 xv = lds8(xa + (uint32_t)l16 * 8u);
   const uint32_t G = U.s[1];
   const float mu = h2f(G);
   const float dl = h2f(G >> 16);
   const float mub = fmaf(-S::kBias, dl, mu);   // radius = (2^(16-L) + q) * delta + mub
   const uint32_t Xh = rotr(U.s[0], half << 4);  // this half's four high sign nibbles at bits 0..15
   const uint32_t expo = S::kExpo;
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  auto pair = [&](auto mc) {
+    constexpr int m = decltype(mc)::value;
     const uint32_t P = U.p[m];
     const uint32_t R = rotr(P, 14);                              // b's fields at a's positions
     const uint32_t ka = P & S::kKeyMask;                         // T[0][s_a lo][z_a]
@@ -195,50 +214,52 @@ __device__ __forceinline__ float decode_unit(const Unit& U, uint32_t half, uint3
     const uint32_t hb = bfi(S::kSignMask, rotr(P, 28 - L), kb);                 // s_b hi
     const float qa = __uint_as_float(and_or(P, S::kQMask, expo));
     const float qb = __uint_as_float(and_or(R, S::kQMask, expo));
-    {
-      const u32x2 lo = lds8(ka);
-      const u32x2 hi = lds8(ha + S::kTHi);
-      const u32x4 xv = lds16(xa + 32u * m);
-      float t = dot2_z(lo[0], xv[0]);
-      t = dot2(lo[1], xv[1], t);
-      t = dot2(hi[0], xv[2], t);
-      t = dot2(hi[1], xv[3], t);
-      acc = fmaf(fmaf(qa, dl, mub), t, acc);
-    }
-    {
-      const u32x2 lo = lds8(kb);
-      const u32x2 hi = lds8(hb + S::kTHi);
-      const u32x4 xv = lds16(xa + 32u * m + 16u);
-      float t = dot2_z(lo[0], xv[0]);
-      t = dot2(lo[1], xv[1], t);
-      t = dot2(hi[0], xv[2], t);
-      t = dot2(hi[1], xv[3], t);
-      acc = fmaf(fmaf(qb, dl, mub), t, acc);
-    }
-  }
+    const float ta = dot8_row<2 * m>(lds8(ka), lds8(ha + S::kTHi), xv[0], xv[1]);
+    acc = fmaf(fmaf(qa, dl, mub), ta, acc);
+    const float tb = dot8_row<2 * m + 1>(lds8(kb), lds8(hb + S::kTHi), xv[0], xv[1]);
+    acc = fmaf(fmaf(qb, dl, mub), tb, acc);
+  };
+  pair(std::integral_constant<int, 0>{});
+  pair(std::integral_constant<int, 1>{});
+  pair(std::integral_constant<int, 2>{});
+  pair(std::integral_constant<int, 3>{});
   return acc;
 }
 
-// Sum of v over each aligned group of tau lanes (tau a power of two up to 64), left in the group's
-// last lane, by a fixed sequence of cross-lane (DPP) additions: pairs, quads, eights (half-row
-// mirror), rows (row mirror), then rows carried forward through row broadcasts.
-template <int kCtrl, int kRowMask>
-__device__ inline float dpp_add(float v) {
-  const float t = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-      0, __builtin_bit_cast(int, v), kCtrl, kRowMask, 0xF, false));
-  return v + t;
-}
-__device__ inline float group_sum(float v, int tau) {
-  if (tau >= 2) v = dpp_add<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
-  if (tau >= 4) v = dpp_add<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
-  if (tau >= 8) v = dpp_add<0x141, 0xF>(v);   // row_half_mirror
-  if (tau >= 16) v = dpp_add<0x140, 0xF>(v);  // row_mirror
-  if (tau >= 32) v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
-  if (tau >= 64) v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
-  return v;
+// The packed units of one lane group, in issue order: unit k of the range is (chunk cf, half-group
+// hf + k) while k < kb, then (chunk cf + 1, half-group k - kb). The cursor holds the byte offsets
+// of the next unit to request; stepping to the following half-group adds 1024 bytes (plane A to
+// plane B of one block) or 1536 (plane B to plane A of the next block), and the side-plane offset
+// moves with the block.
+struct Cursor {
+  uint32_t p, s;     // payload and side offsets of the next unit
+  uint32_t p1, s1;   // the same at half-group 0 of the range's second chunk
+  int hg, k;         // its half-group and index in the range
+};
+
+__device__ inline void cursor_step(Cursor& c, int nh) {
+  const bool odd = (c.hg & 1) != 0;
+  c.hg += 1;
+  c.k += 1;
+  if (c.hg == nh) {
+    c.hg = 0;
+    c.p = c.p1;
+    c.s = c.s1;
+  } else {
+    c.p += odd ? 1536u : 1024u;
+    c.s += odd ? 2560u : 0u;
+  }
 }
 
 // The whole workgroup: chunks [c0, c0 + nc) of one product. kGather: pi may be non-NULL.
+//
+// Order of work. The codebook (in registers of waves 0-3) and the input (in LDS) are waited for
+// first, and the table is written, before any packed unit is requested: a compute unit returns
+// load data in request order across its waves, so small loads queued behind the packed stream
+// would arrive only with it, and a wave whose requests wait for the memory pipeline to accept them
+// would hold every other wave at a later barrier. Each wave then requests its units and decodes
+// them as they land. Every VALU instruction outside the decode loop runs on all 16 wavefronts, so
+// the per-thread set-up is kept short and done while the first loads are in flight.
 template <int L, bool kGather>
 __device__ __attribute__((always_inline)) void gemv_wg(const uint8_t* packed, const uint16_t* codebook, const int32_t* pi,
                         const uint16_t* x, uint16_t* y, int d_out, int d_in, int c0, int nc) {
@@ -246,18 +267,19 @@ __device__ __attribute__((always_inline)) void gemv_wg(const uint8_t* packed, co
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int lg = tid >> 4;
   const int l16 = tid & 15;
+  const int rw = tid >> 4;   // this lane group, and its range
   const int nh = d_in >> 6;   // half-groups per row
   const int ng = d_in >> 7;   // groups per row
+  const int nu = nc * nh;     // units of the workgroup
   const bool gather = kGather && pi != nullptr;
   const uint32_t XB = lds_x(L);
   const uint32_t XS = lds_xs(L, d_in);
   const uint32_t PB = lds_part(L, d_in, gather);
 
-  // 1. Small loads first. Waves 0-3 each load the whole codebook into registers (lane l holds
-  // codewords l, l + 64, ...): four requests per workgroup for data every workgroup shares. The
-  // input (and pi) go straight into LDS, 1 KiB per wave and load.
+  // 1. Small loads. Waves 0-3 each load the whole codebook into registers (lane l holds codewords
+  // l, l + 64, ...): four requests per workgroup for data every workgroup shares. The input (and
+  // pi) go straight into LDS, 1 KiB per wave and load.
   constexpr int kCwPerLane = (int)((S::kK + 63u) / 64u);
   u32x4 cw[kCwPerLane];
   if (wave < 4) {
@@ -276,7 +298,7 @@ __device__ __attribute__((always_inline)) void gemv_wg(const uint8_t* packed, co
     for (int b = wave; b < nkb; b += kThreads / 64)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           x_rs, (__attribute__((address_space(3))) void*)(size_t)(dst + (uint32_t)b * 1024u), 16,
-          (uint32_t)b * 1024u + (uint32_t)(tid & 63) * 16u, 0, 0, 0);
+          (uint32_t)b * 1024u + (uint32_t)lane * 16u, 0, 0, 0);
     if (gather) {
       const __amdgpu_buffer_rsrc_t pi_rs = view(pi, (uint32_t)d_in * 4u);
       const uint32_t PI = lds_pi(L, d_in);
@@ -284,42 +306,38 @@ __device__ __attribute__((always_inline)) void gemv_wg(const uint8_t* packed, co
       for (int b = wave; b < npb; b += kThreads / 64)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             pi_rs, (__attribute__((address_space(3))) void*)(size_t)(PI + (uint32_t)b * 1024u), 16,
-            (uint32_t)b * 1024u + (uint32_t)(tid & 63) * 16u, 0, 0, 0);
+            (uint32_t)b * 1024u + (uint32_t)lane * 16u, 0, 0, 0);
     }
   }
-  __builtin_amdgcn_sched_barrier(0);
 
-  // 2. The lane group's packed units: the first kRing go out now.
-  const LaneWork W = lane_work(lg, nc, nh);
-  const int nu = nc * nh;
-  const int cntw = __builtin_amdgcn_readfirstlane((nu >> 6) + ((nu & 63) > 4 * wave ? 1 : 0));
+  // 2. While those are in flight: this lane group's range and the offsets of its first unit.
+  const LaneWork W = lane_work(rw, nu, nh, __builtin_amdgcn_rcpf((float)nh));
+  // units this wave steps through: the longest range among its four lane groups (range 4 wave)
+  const int cntw = __builtin_amdgcn_readfirstlane((nu >> 6) + (4 * wave < (nu & 63) ? 1 : 0));
   const int tile0 = c0 >> 2;
   const int tiles = ((c0 + nc - 1) >> 2) - tile0 + 1;
   const __amdgpu_buffer_rsrc_t wv =
       view(packed + (size_t)tile0 * ng * kBlockBytes, (uint32_t)tiles * ng * kBlockBytes);
-  // offsets of unit k of this lane: payload (16 bytes) and side (8 bytes)
-  auto unit_off = [&](int k, uint32_t* po, uint32_t* so) {
-    const bool seg1 = k >= W.kb;
-    const int c = c0 + W.cf + (seg1 ? 1 : 0);
-    const int hg = W.hf + k - (seg1 ? nh : 0);
-    const uint32_t lit = (uint32_t)(((c & 3) << 4) | l16);
-    const uint32_t blk = (uint32_t)(((c >> 2) - tile0) * ng + (hg >> 1)) * kBlockBytes;
-    const bool ok = k < W.cnt;
-    *po = ok ? blk + (uint32_t)(hg & 1) * 1024u + lit * 16u : kNowhere;
-    *so = ok ? blk + (uint32_t)kSidePlane + lit * 8u : kNowhere;
-  };
-  Unit ring[kRing];
-#pragma unroll
-  for (int k = 0; k < kRing; ++k) {
-    uint32_t po, so;
-    unit_off(k, &po, &so);
-    ring[k].p = __builtin_amdgcn_raw_buffer_load_b128(wv, po, 0, kNonTemporal);
-    ring[k].s = __builtin_amdgcn_raw_buffer_load_b64(wv, so, 0, kNonTemporal);
+  Cursor cur;
+  {
+    const uint32_t tile_bytes = (uint32_t)ng * kBlockBytes;
+    const int ca = c0 + W.cf, cb = ca + 1;
+    const uint32_t la = (uint32_t)(((ca & 3) << 4) | l16), lb = (uint32_t)(((cb & 3) << 4) | l16);
+    const uint32_t ta = (uint32_t)((ca >> 2) - tile0) * tile_bytes + (uint32_t)(W.hf >> 1) * kBlockBytes;
+    const uint32_t tb = (uint32_t)((cb >> 2) - tile0) * tile_bytes;
+    cur.p = ta + (uint32_t)(W.hf & 1) * 1024u + la * 16u;
+    cur.s = ta + (uint32_t)kSidePlane + la * 8u;
+    cur.p1 = tb + lb * 16u;
+    cur.s1 = tb + (uint32_t)kSidePlane + lb * 8u;
+    cur.hg = W.hf;
+    cur.k = 0;
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 
   // 3. LDS set-up: waves 0-3 write the sign-applied codeword table (wave w the (half, signs)
-  // combinations w, w + 4, ..., for every codeword it holds), then (gathering) the input is
-  // gathered into stored order.
+  // combinations w, w + 4, ..., for every codeword it holds); gathering, every thread puts input
+  // pieces into stored order.
   if (wave < 4) {
 #pragma unroll
     for (int i = 0; i < kCwPerLane; ++i) {
@@ -338,11 +356,8 @@ __device__ __attribute__((always_inline)) void gemv_wg(const uint8_t* packed, co
       }
     }
   }
-  // every load but this wave's packed units has landed (the input pieces included)
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kRing) : "memory");
   if constexpr (kGather) {
     if (gather) {
-      __syncthreads();
       const uint32_t PI = lds_pi(L, d_in);
 #pragma unroll
       for (int i = 0; i < kXIter; ++i) {
@@ -369,68 +384,65 @@ __device__ __attribute__((always_inline)) void gemv_wg(const uint8_t* packed, co
   }
   __syncthreads();
 
-  // 4. Decode: kRing units in flight; unit k + kRing is requested once unit k is decoded.
+  // 4. The packed units: kRing per lane group in flight; unit k + kRing is requested once unit k
+  // is decoded. Units past the range read as zeros (their grid is zero, so they add exactly 0).
+  auto request = [&](Unit& u) {
+    const bool ok = cur.k < W.cnt;
+    u.p = __builtin_amdgcn_raw_buffer_load_b128(wv, ok ? cur.p : kNowhere, 0, kNonTemporal);
+    u.s = __builtin_amdgcn_raw_buffer_load_b64(wv, ok ? cur.s : kNowhere, 0, kNonTemporal);
+    cursor_step(cur, nh);
+  };
+  Unit ring[kRing];
+#pragma unroll
+  for (int k = 0; k < kRing; ++k) request(ring[k]);
+  // a range shorter than its wave's longest steps past its end (zeros); only a range that really
+  // crosses into a second chunk switches sums
+  const bool split = W.kb < W.cnt;
   float acc = 0.0f, acc0 = 0.0f;
+  int dh = W.hf;   // half-group of the unit being decoded
   for (int kk = 0; kk < cntw; kk += kRing) {
 #pragma unroll
     for (int d = 0; d < kRing; ++d) {
       const int k = kk + d;
       if (k < cntw) {
-        const bool seg1 = k >= W.kb;
-        if (k == W.kb) {   // the range enters its second chunk
+        if (split && k == W.kb) {   // the range enters its second chunk
           acc0 = acc;
           acc = 0.0f;
+          dh = 0;
         }
-        const int hg = W.hf + k - (seg1 ? nh : 0);
-        // input of the unit's 8 subvectors (units past the lane's range read position 0)
-        const uint32_t xa = XB + (k < W.cnt ? (uint32_t)hg * 128u : 0u);
-        acc = decode_unit<L>(ring[d], (uint32_t)hg & 1u, xa, acc);
-        if (k + kRing < cntw) {
-          uint32_t po, so;
-          unit_off(k + kRing, &po, &so);
-          ring[d].p = __builtin_amdgcn_raw_buffer_load_b128(wv, po, 0, kNonTemporal);
-          ring[d].s = __builtin_amdgcn_raw_buffer_load_b64(wv, so, 0, kNonTemporal);
-        }
+        const uint32_t xa = XB + (uint32_t)min(dh, nh - 1) * 128u;
+        acc = decode_unit<L>(ring[d], (uint32_t)dh & 1u, xa, l16, acc);
+        dh += 1;
+        if (k + kRing < cntw) request(ring[d]);
       }
     }
   }
 
-  // 5. Lane-group sums to LDS; then the lane groups that worked on a chunk (a contiguous run
-  // lo..hi) are added for each of its rows: tau threads per row take every tau-th contributor in
-  // order and a fixed cross-lane tree adds their sums (results reproducible bit for bit).
-  const bool split = W.kb < W.cnt;   // the range covers two chunks
+  // 5. Range sums to LDS (slot 0: the range's first chunk, slot 1: its second), then one thread
+  // per row adds the sums of the ranges that cover its chunk (a contiguous run lo..hi) in range
+  // order: a fixed order, so results are reproducible bit for bit.
   {
-    const uint32_t a = PB + (uint32_t)(lg * kChunkRows + l16) * 4u;
+    const uint32_t a = PB + (uint32_t)(rw * kChunkRows + l16) * 4u;
     *(__attribute__((address_space(3))) float*)(size_t)a = split ? acc0 : acc;
     *(__attribute__((address_space(3))) float*)(size_t)(a + kLaneGroups * kChunkRows * 4u) =
         split ? acc : 0.0f;
   }
   __syncthreads();
-  {
-    const int rows = nc * kChunkRows;
-    // threads per row: 64 for one chunk, halving as chunks are added (a power of two dividing 64)
-    const int tau = rows <= 16 ? 64 : rows <= 32 ? 32 : rows <= 64 ? 16 : rows <= 128 ? 8
-                  : rows <= 256 ? 4 : rows <= 512 ? 2 : 1;
-    const int r = tid / tau, k = tid & (tau - 1);
-    float sum = 0.0f;
-    if (r < rows) {
-      const int cl = r >> 4, rr = r & 15;
-      const int base = nu >> 6, rem = nu & 63;
-      const int lo = lane_group_of(cl * nh, base, rem);
-      const int hi = lane_group_of((cl + 1) * nh - 1, base, rem);
-      // lo may have started in the previous chunk: its sum for this chunk is its second one
-      const bool lo_second = lo * base + min(lo, rem) < cl * nh;
-      for (int g = lo + k; g <= hi; g += tau) {
-        const uint32_t seg = (g == lo && lo_second) ? 1u : 0u;
-        sum += *(__attribute__((address_space(3))) const float*)(size_t)(
-            PB + ((seg * kLaneGroups + (uint32_t)g) * kChunkRows + (uint32_t)rr) * 4u);
-      }
-    }
-    sum = group_sum(sum, tau);
-    if (r < rows && k == tau - 1) {
-      const int row = (c0 + (r >> 4)) * kChunkRows + (r & 15);
-      if (row < d_out) y[row] = f2h(sum);
-    }
+  if (tid < nc * kChunkRows) {
+    const int cl = tid >> 4, rr = tid & 15;
+    const int base = nu >> 6, rem = nu & 63;
+    const int ub = cl * nh;   // the chunk's first unit
+    const int lo = range_of(ub, base, rem);
+    const int hi = range_of(ub + nh - 1, base, rem);
+    // lo may have started in the previous chunk: its sum for this chunk is its second one
+    const uint32_t seg = lo * base + min(lo, rem) < ub ? 1u : 0u;
+    typedef __attribute__((address_space(3))) const float lds_f;
+    float sum = *(lds_f*)(size_t)(PB + ((seg * kLaneGroups + (uint32_t)lo) * kChunkRows + rr) * 4u);
+#pragma unroll 8
+    for (int g = lo + 1; g <= hi; ++g)
+      sum += *(lds_f*)(size_t)(PB + ((uint32_t)g * kChunkRows + (uint32_t)rr) * 4u);
+    const int row = (c0 + cl) * kChunkRows + rr;
+    if (row < d_out) y[row] = f2h(sum);
   }
 }
 

@@ -281,6 +281,32 @@ def test_gemv_multi_many_chunks(rows, d_in):
         assert np.array_equal(_np(y), f), "repeat call must reproduce the same bits"
 
 
+def test_gemv_range_padding_at_chunk_end():
+    """Single-chunk products for every even half-group count mod 64 (d_in = 64 * 2..128): the 64
+    lane-group ranges then differ in length by one, a range shorter than the longest in its
+    wavefront steps one unit past its end, and where such a range ends exactly at the chunk's end
+    that padding step must leave its sum where it is."""
+    rng = W.rng_for(140)
+    for d_out in (16, 9):
+        for nhalf in range(2, 130, 2):
+            d_in = 64 * nhalf
+            c = W.draw_codes(rng, d_out, d_in, 64, 4)
+            x = W.draw_x(rng, (d_in,))
+            y = sage.gemv(upload_pack(c), _dev(x))
+            check_gemv(f"one chunk {d_out}x{d_in}", c, x, y)
+
+
+@pytest.mark.parametrize("d_in", [2560, 3968])
+def test_gemv_range_padding_two_and_three_chunks(d_in):
+    """8784 rows = 549 chunks: two or three chunks per workgroup on a 256-CU device, ranges that
+    cross a chunk boundary next to ranges that end exactly at one."""
+    rng = W.rng_for(141, d_in)
+    c = W.draw_codes(rng, 8784, d_in, 64, 4)
+    x = W.draw_x(rng, (d_in,))
+    y = sage.gemv(upload_pack(c), _dev(x))
+    check_gemv(f"chunks 8784x{d_in}", c, x, y)
+
+
 def test_gemv_most_chunks_per_workgroup():
     """One product with more than 64 chunks per compute unit: the planner adds workgroups (each
     takes at most 64 chunks, 1024 rows)."""
