@@ -4,19 +4,18 @@
 Default workload: one Qwen3-4B-shaped decoder layer at batch one (q 4096x2560, k/v 1024x2560,
 o 2560x4096, gate/up 9728x2560, down 2560x9728), split (K, V) = (64, 4), codes drawn directly
 (synthetic, seeded). A step is one pass over the layer's seven projections in dependency order:
-q|k|v in one launch (they read the same input), o, gate|up in one launch, down (with --fused, the
-SwiGLU block gate, up, silu*mul, down is one sage_mlp launch). Every step uses a different copy of
-the layer's packed weights, and the copies together exceed 512 MB, twice the MI355X's 256 MB
-last-level cache, so weights stream from HBM as they would in a model.
+q|k|v in one launch (they read the same input), o, gate|up in one launch, down. Every step uses a
+different copy of the layer's packed weights, and the copies together exceed 512 MB, twice the
+MI355X's 256 MB last-level cache, so weights stream from HBM as they would in a model.
 
 The timed region replays a HIP graph of the steps (launching from Python per kernel would measure
 the host, not the GPU). It prints one JSON line: whole-step packed-weight GB/s (the metric), the
-per-step time, tokens/s of the layer, the roofline of the dominant launch (gate|up, or the fused
-block) from HIP events around a graph of such launches on their stream, the HBM traffic measured
-with counters (profiles/), a plain streaming read of the same bytes as the reference floor, and
+per-step time, tokens/s of the layer, the roofline of the dominant launch (gate|up) from HIP
+events around a graph of such launches on their stream, the HBM traffic measured with counters
+(profiles/), a plain streaming read of the same bytes as the reference floor, and
 the CPU oracle's rate on a bounded sample of the same workload.
 
-  python bench.py [--steps K] [--warmup W] [--fused]
+  python bench.py [--steps K] [--warmup W] [--mode compiled|eager]
                   [--workload layer|sweep|gemm|prefill|moe|encode|single|all]
 
 The secondary workloads print one JSON line per case (not the headline line); `encode` times the
@@ -100,7 +99,7 @@ def packed_weight_bytes(p):
     return p.d_out * p.d_in * 18 // 64 + p.d_out * (p.d_in // 128) * 4
 
 
-GEMV_SOURCES = ("sage_gemv.hip", "sage_gemv.hpp", "sage_internal.hpp")
+GEMV_SOURCES = ("sage_gemv.hip", "sage_internal.hpp")
 
 
 def kernel_sources_digest():
