@@ -4,9 +4,9 @@
 // Work decomposition. Rows are taken in chunks of 16 (a quarter of a packed row tile). A workgroup
 // of 1024 threads (16 wavefronts, one workgroup per compute unit) owns whole rows: a run of chunks
 // of one product, so no partial sum ever leaves the compute unit (no split-K hand-off between
-// workgroups). Its (chunk, half-group) units, chunk-major, are cut into 64 contiguous ranges whose
-// lengths differ by at most one, one per lane group of 16 lanes; lane l of a group owns row l of
-// the chunk it is working on. A range crosses at most one chunk boundary, so a lane keeps two sums.
+// workgroups). Its (chunk, 128-column group) units, chunk-major, are cut into 64 contiguous ranges
+// whose lengths differ by at most one, one per lane group of 16 lanes; lane l of a group owns row l
+// of the chunk it is working on. A range crosses at most one chunk boundary, so a lane keeps two sums.
 // At the end one thread per row adds the sums of the ranges covering its chunk in range order (a
 // fixed order: results are reproducible bit for bit) and one rounding to fp16 gives y.
 //
@@ -17,16 +17,16 @@
 // position. A subvector then costs two 8-byte table reads, addressed straight from bit fields of
 // the packed word (the packed layout puts z and each sign nibble next to each other), four fp16
 // dot2 steps with fp32 accumulation against the input, and the radius mu + q*delta applied once
-// to the 8-term dot product (App. A.1: one multiply instead of eight). The input is staged in LDS
+// to the 8-term dot product (App. A.1: one multiply instead of eight). Lane j of a lane group reads
+// the inputs of the unit's subvector j from LDS once, and every lane of the group takes them from
+// lane j through a DPP row broadcast inside the dot steps. The input is staged in LDS
 // in stored (permuted) column order: copied as is when the matrix's pi is NULL (the producer wrote
 // it permuted, §3.5 compiled decoding), else gathered through pi once per workgroup (§3.5 eager
 // decoding: the gather fused into the product).
 //
 // Memory access. Every global load is a buffer load through a range-checked view: loads past the
-// range return zeros without a memory access, so loads are issued unconditionally (units a lane
-// group does not own decode as zeros: their grid is zero, so they add exactly 0). The codebook and
-// input loads go out first, then the packed units of every lane group; four units per lane group
-// stay in flight while it decodes.
+// range return zeros without a memory access, so loads are issued unconditionally. The codebook
+// and input land first; then every lane group requests its units, two in flight while it decodes.
 #include <algorithm>
 #include <mutex>
 #include <vector>
@@ -44,7 +44,7 @@ constexpr int kThreads = 1024;
 constexpr int kLaneGroups = 64;
 constexpr int kChunkRows = 16;
 constexpr int kMaxChunks = 64;     // chunks per workgroup (a lane-group range stays within 2)
-constexpr int kRing = 4;           // half-group units in flight per lane group
+constexpr int kRing = 2;           // group units in flight per lane group
 constexpr int kMaxProducts = 16;
 constexpr int kMaxWgs = 768;
 constexpr int kMaxDin = 32768;     // widest input staged whole in LDS (stored order)
@@ -135,8 +135,11 @@ struct Split {
   static constexpr uint32_t kTHi = 128u << L;   // second-half table
 };
 
+// One unit of work: a lane group's 16 rows (one chunk) by one 128-column group, i.e. each lane's
+// three pieces of one packed block.
 struct Unit {
-  u32x4 p;  // payload dwords of the half-group (one plane)
+  u32x4 a;  // payload dwords P0..P3 of the lane's row (plane A)
+  u32x4 b;  // P4..P7 (plane B)
   u32x2 s;  // X, G
 };
 
@@ -144,22 +147,22 @@ struct Unit {
 // d lies at least 1/(2d) from every integer, and the float product's error is below (n/d) 2^-21.
 __device__ inline int div_small(int n, float r) { return (int)(((float)n + 0.5f) * r); }
 
-// Per lane-group work. A workgroup's units (chunk, half-group), chunk-major, are split into 64
+// Per lane-group work. A workgroup's units (chunk, group), chunk-major, are split into 64
 // contiguous ranges, range w for lane group w (so a wavefront's four ranges are neighbours and
 // differ in length only where the longer ranges end). Range w is units [u0, u0 + cnt); its first
-// kb units lie in chunk cf (half-groups hf, hf + 1, ...), the rest in chunk cf + 1.
+// kb units lie in chunk cf (groups gf, gf + 1, ...), the rest in chunk cf + 1.
 struct LaneWork {
-  int u0, cnt, cf, hf, kb;
+  int u0, cnt, cf, gf, kb;
 };
 
-__device__ inline LaneWork lane_work(int w, int nu, int nh, float rcp_nh) {
+__device__ inline LaneWork lane_work(int w, int nu, int ng, float rcp_ng) {
   const int base = nu >> 6, rem = nu & 63;
   LaneWork r;
   r.cnt = base + (w < rem ? 1 : 0);
   r.u0 = w * base + min(w, rem);
-  r.cf = div_small(r.u0, rcp_nh);
-  r.hf = r.u0 - r.cf * nh;
-  r.kb = nh - r.hf;
+  r.cf = div_small(r.u0, rcp_ng);
+  r.gf = r.u0 - r.cf * ng;
+  r.kb = ng - r.gf;
   return r;
 }
 // Range holding unit u (inverse of the split above).
@@ -170,85 +173,69 @@ __device__ inline int range_of(int u, int base, int rem) {
                  : rem + div_small(u - big, __builtin_amdgcn_rcpf((float)base));
 }
 
-// Dot product of one subvector's 8 sign-applied codeword values (lo, hi: four fp16 pairs) with its
-// 8 inputs, which lanes 2j and 2j + 1 of the lane group hold (two fp16 pairs each). The lane group
-// is a DPP row of 16 lanes, and row_newbcast hands every lane of the row the given lane's register
-// as the dot's first operand: no LDS traffic for the input. The leading s_nop gives the two wait
-// states a DPP read needs after a VALU write of its source (the inputs come from an LDS read, but
-// the block does not rely on that).
+// acc += r * (c . x) for one subvector: c its 8 sign-applied codeword values (lo, hi: four fp16
+// pairs), x its 8 inputs, all four fp16 pairs of which lane J of the lane group holds, r its radius.
+// The lane group is a DPP row of 16 lanes, and row_newbcast hands every lane of the row lane J's
+// register as the dot's first operand: no LDS traffic for the input. The dot product starts from 0
+// and accumulates in fp32; the radius multiply-add follows in the same block, so each subvector is
+// added in order and its dot product does not stay live.
+//
+// Wait states the compiler cannot insert, the dot steps being inside the block: the leading s_nop
+// gives the two a DPP read needs after a VALU write of its source (the inputs come from LDS reads,
+// but the block does not rely on that); the s_nop 2 gives the three a VALU read needs after a
+// v_dot2c write of the value (a dot step reading it as its own accumulator needs none). Row
+// broadcasts run with every lane active: under a partial exec mask they gave wrong sums.
 template <int J>
-__device__ __forceinline__ float dot8_row(u32x2 lo, u32x2 hi, uint32_t x0, uint32_t x1) {
+__device__ __forceinline__ float dot8_row(float acc, float r, u32x2 lo, u32x2 hi, u32x4 xv) {
   float t;
   asm("s_nop 1\n\t"
-      "v_mov_b32 %0, 0\n\t"
-      "v_dot2c_f32_f16_dpp %0, %5, %1 row_newbcast:%7 row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_f16_dpp %0, %6, %2 row_newbcast:%7 row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_f16_dpp %0, %5, %3 row_newbcast:%8 row_mask:0xf bank_mask:0xf\n\t"
-      "v_dot2c_f32_f16_dpp %0, %6, %4 row_newbcast:%8 row_mask:0xf bank_mask:0xf"
-      : "=&v"(t)
-      : "v"(lo[0]), "v"(lo[1]), "v"(hi[0]), "v"(hi[1]), "v"(x0), "v"(x1), "n"(2 * J),
-        "n"(2 * J + 1));
-  return t;
+      "v_mov_b32 %1, 0\n\t"
+      "v_dot2c_f32_f16_dpp %1, %7, %3 row_newbcast:%11 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_f16_dpp %1, %8, %4 row_newbcast:%11 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_f16_dpp %1, %9, %5 row_newbcast:%11 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_f16_dpp %1, %10, %6 row_newbcast:%11 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 2\n\t"
+      "v_fmac_f32 %0, %2, %1"
+      : "+v"(acc), "=&v"(t)
+      : "v"(r), "v"(lo[0]), "v"(lo[1]), "v"(hi[0]), "v"(hi[1]), "v"(xv[0]), "v"(xv[1]),
+        "v"(xv[2]), "v"(xv[3]), "n"(J));
+  return acc;
 }
 
-// Decode the 8 subvectors of one half-group unit and add them to acc. xa: LDS address of the
-// unit's 64 inputs; lane l of the lane group reads inputs 4l .. 4l + 3.
+// Decode the 16 subvectors of one unit and add them to acc. xa: LDS address of the group's 128
+// inputs; lane l of the lane group reads inputs 8l .. 8l + 7 (subvector l's).
 template <int L>
-__device__ __forceinline__ float decode_unit(const Unit& U, uint32_t half, uint32_t xa, int l16,
-                                             float acc) {
+__device__ __forceinline__ float decode_unit(const Unit& U, uint32_t xa, int l16, float acc) {
   using S = Split<L>;
-  const u32x2 xv = lds8(xa + (uint32_t)l16 * 8u);
+  const u32x4 xv = lds16(xa + (uint32_t)l16 * 16u);
+  const uint32_t X = U.s[0];
   const uint32_t G = U.s[1];
   const float mu = h2f(G);
   const float dl = h2f(G >> 16);
   const float mub = fmaf(-S::kBias, dl, mu);   // radius = (2^(16-L) + q) * delta + mub
-  const uint32_t Xh = rotr(U.s[0], half << 4);  // this half's four high sign nibbles at bits 0..15
   const uint32_t expo = S::kExpo;
   auto pair = [&](auto mc) {
     constexpr int m = decltype(mc)::value;
-    const uint32_t P = U.p[m];
+    const uint32_t P = m < 4 ? U.a[m & 3] : U.b[m & 3];
     const uint32_t R = rotr(P, 14);                              // b's fields at a's positions
     const uint32_t ka = P & S::kKeyMask;                         // T[0][s_a lo][z_a]
     const uint32_t kb = R & S::kKeyMask;                         // T[0][s_b lo][z_b]
-    const uint32_t ha = bfi(S::kSignMask, rotr(Xh, (4 * m + 29 - L) & 31), ka);  // s_a hi
-    const uint32_t hb = bfi(S::kSignMask, rotr(P, 28 - L), kb);                 // s_b hi
+    const uint32_t ha = bfi(S::kSignMask, rotr(X, (4 * m + 29 - L) & 31), ka);  // s_a hi
+    const uint32_t hb = bfi(S::kSignMask, rotr(P, 28 - L), kb);                // s_b hi
     const float qa = __uint_as_float(and_or(P, S::kQMask, expo));
     const float qb = __uint_as_float(and_or(R, S::kQMask, expo));
-    const float ta = dot8_row<2 * m>(lds8(ka), lds8(ha + S::kTHi), xv[0], xv[1]);
-    acc = fmaf(fmaf(qa, dl, mub), ta, acc);
-    const float tb = dot8_row<2 * m + 1>(lds8(kb), lds8(hb + S::kTHi), xv[0], xv[1]);
-    acc = fmaf(fmaf(qb, dl, mub), tb, acc);
+    acc = dot8_row<2 * m>(acc, fmaf(qa, dl, mub), lds8(ka), lds8(ha + S::kTHi), xv);
+    acc = dot8_row<2 * m + 1>(acc, fmaf(qb, dl, mub), lds8(kb), lds8(hb + S::kTHi), xv);
   };
   pair(std::integral_constant<int, 0>{});
   pair(std::integral_constant<int, 1>{});
   pair(std::integral_constant<int, 2>{});
   pair(std::integral_constant<int, 3>{});
+  pair(std::integral_constant<int, 4>{});
+  pair(std::integral_constant<int, 5>{});
+  pair(std::integral_constant<int, 6>{});
+  pair(std::integral_constant<int, 7>{});
   return acc;
-}
-
-// The packed units of one lane group, in issue order: unit k of the range is (chunk cf, half-group
-// hf + k) while k < kb, then (chunk cf + 1, half-group k - kb). The cursor holds the byte offsets
-// of the next unit to request; stepping to the following half-group adds 1024 bytes (plane A to
-// plane B of one block) or 1536 (plane B to plane A of the next block), and the side-plane offset
-// moves with the block.
-struct Cursor {
-  uint32_t p, s;     // payload and side offsets of the next unit
-  uint32_t p1, s1;   // the same at half-group 0 of the range's second chunk
-  int hg, k;         // its half-group and index in the range
-};
-
-__device__ inline void cursor_step(Cursor& c, int nh) {
-  const bool odd = (c.hg & 1) != 0;
-  c.hg += 1;
-  c.k += 1;
-  if (c.hg == nh) {
-    c.hg = 0;
-    c.p = c.p1;
-    c.s = c.s1;
-  } else {
-    c.p += odd ? 1536u : 1024u;
-    c.s += odd ? 2560u : 0u;
-  }
 }
 
 // The whole workgroup: chunks [c0, c0 + nc) of one product. kGather: pi may be non-NULL.
@@ -269,9 +256,8 @@ __device__ __attribute__((always_inline)) void gemv_wg(const uint8_t* packed, co
   const int lane = tid & 63;
   const int l16 = tid & 15;
   const int rw = tid >> 4;   // this lane group, and its range
-  const int nh = d_in >> 6;   // half-groups per row
   const int ng = d_in >> 7;   // groups per row
-  const int nu = nc * nh;     // units of the workgroup
+  const int nu = nc * ng;     // units of the workgroup
   const bool gather = kGather && pi != nullptr;
   const uint32_t XB = lds_x(L);
   const uint32_t XS = lds_xs(L, d_in);
@@ -310,27 +296,32 @@ __device__ __attribute__((always_inline)) void gemv_wg(const uint8_t* packed, co
     }
   }
 
-  // 2. While those are in flight: this lane group's range and the offsets of its first unit.
-  const LaneWork W = lane_work(rw, nu, nh, __builtin_amdgcn_rcpf((float)nh));
+  // 2. While those are in flight: this lane group's range and the offsets of its units. Unit k
+  // of the range is (chunk cf, group gf + k) for k < kb, then (chunk cf + 1, group k - kb); both
+  // runs step 2560 bytes (one block) per unit, so unit k sits at base + 2560 k with the base of
+  // its run (the second run's base shifted back by kb blocks).
+  const LaneWork W = lane_work(rw, nu, ng, __builtin_amdgcn_rcpf((float)ng));
   // units this wave steps through: the longest range among its four lane groups (range 4 wave)
   const int cntw = __builtin_amdgcn_readfirstlane((nu >> 6) + (4 * wave < (nu & 63) ? 1 : 0));
   const int tile0 = c0 >> 2;
   const int tiles = ((c0 + nc - 1) >> 2) - tile0 + 1;
+  const uint32_t tile_bytes = (uint32_t)ng * kBlockBytes;
   const __amdgpu_buffer_rsrc_t wv =
-      view(packed + (size_t)tile0 * ng * kBlockBytes, (uint32_t)tiles * ng * kBlockBytes);
-  Cursor cur;
+      view(packed + (size_t)tile0 * tile_bytes, (uint32_t)tiles * tile_bytes);
+  uint32_t pa0, sa0, pa1, sa1, xa0, xa1;   // payload, side and input offsets of both runs
   {
-    const uint32_t tile_bytes = (uint32_t)ng * kBlockBytes;
     const int ca = c0 + W.cf, cb = ca + 1;
     const uint32_t la = (uint32_t)(((ca & 3) << 4) | l16), lb = (uint32_t)(((cb & 3) << 4) | l16);
-    const uint32_t ta = (uint32_t)((ca >> 2) - tile0) * tile_bytes + (uint32_t)(W.hf >> 1) * kBlockBytes;
-    const uint32_t tb = (uint32_t)((cb >> 2) - tile0) * tile_bytes;
-    cur.p = ta + (uint32_t)(W.hf & 1) * 1024u + la * 16u;
-    cur.s = ta + (uint32_t)kSidePlane + la * 8u;
-    cur.p1 = tb + lb * 16u;
-    cur.s1 = tb + (uint32_t)kSidePlane + lb * 8u;
-    cur.hg = W.hf;
-    cur.k = 0;
+    const uint32_t ta = __umul24((uint32_t)((ca >> 2) - tile0), tile_bytes) +
+                        __umul24((uint32_t)W.gf, (uint32_t)kBlockBytes);
+    const uint32_t tb = __umul24((uint32_t)((cb >> 2) - tile0), tile_bytes) -
+                        __umul24((uint32_t)W.kb, (uint32_t)kBlockBytes);
+    pa0 = ta + la * 16u;
+    sa0 = ta + (uint32_t)kSidePlane + la * 8u;
+    pa1 = tb + lb * 16u;
+    sa1 = tb + (uint32_t)kSidePlane + lb * 8u;
+    xa0 = XB + (uint32_t)W.gf * 256u;
+    xa1 = XB - (uint32_t)W.kb * 256u;
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -385,21 +376,28 @@ __device__ __attribute__((always_inline)) void gemv_wg(const uint8_t* packed, co
   __syncthreads();
 
   // 4. The packed units: kRing per lane group in flight; unit k + kRing is requested once unit k
-  // is decoded. Units past the range read as zeros (their grid is zero, so they add exactly 0).
-  auto request = [&](Unit& u) {
-    const bool ok = cur.k < W.cnt;
-    u.p = __builtin_amdgcn_raw_buffer_load_b128(wv, ok ? cur.p : kNowhere, 0, kNonTemporal);
-    u.s = __builtin_amdgcn_raw_buffer_load_b64(wv, ok ? cur.s : kNowhere, 0, kNonTemporal);
-    cursor_step(cur, nh);
+  // is decoded. A range shorter than its wave's longest steps one unit past its end. That unit is
+  // read as zeros and decoded with every lane active (its zero grid adds exactly 0): the DPP row
+  // broadcasts of the dot steps gave wrong sums when run under a partial exec mask, even with every
+  // lane of the row active. Its inputs are those of the group after the range's last one in the
+  // same chunk, or of group 0 when the range ends at its chunk's end (a range covers at most a
+  // chunk's units, so never the end of a second chunk): always staged, finite inputs.
+  auto request = [&](Unit& u, int k) {
+    const uint32_t step = (uint32_t)k * (uint32_t)kBlockBytes;
+    const bool second = k >= W.kb;
+    const bool ok = k < W.cnt;
+    const uint32_t po = ok ? (second ? pa1 : pa0) + step : kNowhere;
+    const uint32_t so = ok ? (second ? sa1 : sa0) + step : kNowhere;
+    u.a = __builtin_amdgcn_raw_buffer_load_b128(wv, po, 0, kNonTemporal);
+    u.b = __builtin_amdgcn_raw_buffer_load_b128(wv, po + (uint32_t)kPlaneB, 0, kNonTemporal);
+    u.s = __builtin_amdgcn_raw_buffer_load_b64(wv, so, 0, kNonTemporal);
   };
   Unit ring[kRing];
 #pragma unroll
-  for (int k = 0; k < kRing; ++k) request(ring[k]);
-  // a range shorter than its wave's longest steps past its end (zeros); only a range that really
-  // crosses into a second chunk switches sums
+  for (int k = 0; k < kRing; ++k) request(ring[k], k);
+  // only a range that really crosses into a second chunk switches sums
   const bool split = W.kb < W.cnt;
   float acc = 0.0f, acc0 = 0.0f;
-  int dh = W.hf;   // half-group of the unit being decoded
   for (int kk = 0; kk < cntw; kk += kRing) {
 #pragma unroll
     for (int d = 0; d < kRing; ++d) {
@@ -408,12 +406,10 @@ __device__ __attribute__((always_inline)) void gemv_wg(const uint8_t* packed, co
         if (split && k == W.kb) {   // the range enters its second chunk
           acc0 = acc;
           acc = 0.0f;
-          dh = 0;
         }
-        const uint32_t xa = XB + (uint32_t)min(dh, nh - 1) * 128u;
-        acc = decode_unit<L>(ring[d], (uint32_t)dh & 1u, xa, l16, acc);
-        dh += 1;
-        if (k + kRing < cntw) request(ring[d]);
+        const uint32_t xa = (k >= W.kb ? xa1 : xa0) + (uint32_t)k * 256u;
+        acc = decode_unit<L>(ring[d], xa, l16, acc);
+        if (k + kRing < cntw) request(ring[d], k + kRing);
       }
     }
   }
@@ -431,9 +427,9 @@ __device__ __attribute__((always_inline)) void gemv_wg(const uint8_t* packed, co
   if (tid < nc * kChunkRows) {
     const int cl = tid >> 4, rr = tid & 15;
     const int base = nu >> 6, rem = nu & 63;
-    const int ub = cl * nh;   // the chunk's first unit
+    const int ub = cl * ng;   // the chunk's first unit
     const int lo = range_of(ub, base, rem);
-    const int hi = range_of(ub + nh - 1, base, rem);
+    const int hi = range_of(ub + ng - 1, base, rem);
     // lo may have started in the previous chunk: its sum for this chunk is its second one
     const uint32_t seg = lo * base + min(lo, rem) < ub ? 1u : 0u;
     typedef __attribute__((address_space(3))) const float lds_f;
@@ -564,9 +560,14 @@ int plan(const sage_matrix_t* mats, const uint16_t* const* xs, uint16_t* const* 
     total_units += units[i];
     total_chunks += chunks[i];
   }
-  // workgroups: one per compute unit, no more than there are chunks, and at least enough that no
-  // workgroup has more than kMaxChunks chunks
-  int64_t G = std::min<int64_t>(cus, total_chunks);
+  // workgroups: two per compute unit when two fit in its LDS (eight wavefronts per SIMD hide the
+  // latency of the table reads better than four), else one; no more than there are chunks, and at
+  // least enough that no workgroup has more than kMaxChunks chunks
+  uint32_t lds_max = 0;
+  for (int i = 0; i < n; ++i)
+    lds_max = std::max(lds_max, lds_total(mats[i].log2K, mats[i].d_in, mats[i].pi != nullptr));
+  const int per_cu = lds_max <= kMaxLds / 2 ? 2 : 1;
+  int64_t G = std::min<int64_t>((int64_t)cus * per_cu, total_chunks);
   std::vector<int64_t> g(n);
   std::vector<std::pair<double, int>> rema;
   int64_t given = 0;
