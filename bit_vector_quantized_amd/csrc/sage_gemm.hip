@@ -208,7 +208,30 @@ __device__ inline uint32_t scale_pair(uint32_t c, float r) {
   return __builtin_bit_cast(uint32_t, half2_t{lo, hi});
 }
 
-// LDS layout: codebook replicas [K][16][16 B], 128 spare bytes, flag, then the X tile
+// One fp16 pair c scaled by r: each half becomes fp16(c_i * r) with a single rounding of the exact
+// product (v_fma_mix takes the fp16 half as its first operand, r in fp32, and rounds the fused
+// result once to fp16: the weight the paper's kernel stores, App. A.1).
+__device__ inline uint32_t scale_pair_mix(uint32_t c, float r) {
+  uint32_t d;
+  asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+      : "=&v"(d)
+      : "v"(c), "v"(r));
+  return d;
+}
+
+// Table entry address of the sign-applied codeword halves (the batch-one kernel's table, built
+// once per workgroup from the codebook): T[h][s][z] at ((h * 16 + s) * K + z) * 8 holds
+// c_z[4h .. 4h+3] with element i negated when bit i of s is set.
+template <int L>
+struct TKeys {
+  static constexpr uint32_t kKeyMask = ((1u << (4 + L)) - 1u) << 3;   // z and a sign nibble
+  static constexpr uint32_t kSignMask = 15u << (3 + L);
+  static constexpr uint32_t kTHi = 128u << L;
+};
+__device__ inline uint32_t rotr32(uint32_t v, uint32_t n) { return __builtin_amdgcn_alignbit(v, v, n); }
+
+// LDS layout: the sign-applied codeword table [256 K bytes], 128 spare bytes, flag, then the X tile
 // [NT*16][gs*128 + 8] fp16 (also the part-sum exchange once the products are done).
 __host__ __device__ inline uint32_t gemm_xs_offset(int L) { return (1u << L) * 256u + 144u; }
 
@@ -303,10 +326,18 @@ __device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint
     }
   }
 
-  // 2. LDS set-up.
+  // 2. LDS set-up: thread z < K writes the 32 sign-applied halves of codeword z.
   if (tid < (int)kK) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) *reinterpret_cast<u32x4*>(cb + tid * 256 + r * 16) = cw;
+    for (int hs = 0; hs < 32; ++hs) {
+      const uint32_t h = (uint32_t)hs >> 4, sg = (uint32_t)hs & 15u;
+      const uint32_t c01 = h ? cw[2] : cw[0];
+      const uint32_t c23 = h ? cw[3] : cw[1];
+      const uint32_t m01 = ((sg & 1u) << 15) | ((sg & 2u) << 30);
+      const uint32_t m23 = ((sg & 4u) << 13) | ((sg & 8u) << 28);
+      *reinterpret_cast<u32x2*>(cb + ((uint32_t)hs * kK + (uint32_t)tid) * 8u) =
+          u32x2{c01 ^ m01, c23 ^ m23};
+    }
   }
   if constexpr (kVec) {
 #pragma unroll
@@ -334,7 +365,6 @@ __device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
   const bool row_ok = tile_ok && wrow < A.d_out;  // padded rows decode to zero weights anyway
-  const uint32_t laneoff = (uint32_t)(lane & 15) * 16u;
   // the SIMD's issue slots go to the oldest wave first; a wave's priority is its remaining groups
   // (3 down to 0), so the four waves of a SIMD advance together instead of one after another
   __builtin_amdgcn_s_setprio(3);
@@ -348,30 +378,34 @@ __device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint
       const int slot = k0 + k;
       const float mu = h2f(sd[k][1]);
       const float dl = h2f(sd[k][1] >> 16);
+      using TK = TKeys<L>;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        // subvector 4u + kk of the group: payload dword 2u + kk/2, half a (kk even) or b (kk odd)
+        // subvector 4u + kk of the group: payload dword 2u + kk/2, half a (kk even) or b (kk odd);
+        // its table keys come straight from the packed word (see the batch-one kernel): the low
+        // sign nibble sits next to z, the high one is rotated into place from X (a) or P (b)
         const uint32_t P = (kk < 2) ? pp[k][0] : pp[k][1];
-        const int pair = 2 * u + (kk >> 1);
-        uint32_t s, z, q;
+        const uint32_t pair = 2u * (uint32_t)u + (uint32_t)(kk >> 1);
+        uint32_t klo, khi, q;
         if ((kk & 1) == 0) {
-          z = (P >> 3) & (kK - 1u);
+          klo = P & TK::kKeyMask;
+          khi = (rotr32(sd[k][0], (4u * pair + 29u - (uint32_t)L) & 31u) & TK::kSignMask) |
+                (klo & ~TK::kSignMask);
           q = (P >> (7 + L)) & ((1u << (10 - L)) - 1u);
-          s = ((P >> (3 + L)) & 15u) | (((sd[k][0] >> (4 * pair)) & 15u) << 4);
         } else {
-          z = (P >> 17) & (kK - 1u);
-          q = (P >> (21 + L)) & ((1u << (10 - L)) - 1u);
-          s = ((P >> (17 + L)) & 15u) | ((P >> 31) << 4) | ((P & 7u) << 5);
+          const uint32_t R = rotr32(P, 14);
+          klo = R & TK::kKeyMask;
+          khi = (rotr32(P, 28 - L) & TK::kSignMask) | (klo & ~TK::kSignMask);
+          q = (R >> (7 + L)) & ((1u << (10 - L)) - 1u);
         }
         const float r = fmaf((float)q, dl, mu);
-        const uint4 c = *reinterpret_cast<const uint4*>(cb + z * 256 + laneoff);
-        const uint2 mlo = sign_masks(s & 15u);
-        const uint2 mhi = sign_masks(s >> 4);
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(cb + klo);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(cb + TK::kTHi + khi);
         uint32_t w[4];
-        w[0] = scale_pair(c.x ^ mlo.x, r);
-        w[1] = scale_pair(c.y ^ mlo.y, r);
-        w[2] = scale_pair(c.z ^ mhi.x, r);
-        w[3] = scale_pair(c.w ^ mhi.y, r);
+        w[0] = scale_pair_mix(lo[0], r);
+        w[1] = scale_pair_mix(lo[1], r);
+        w[2] = scale_pair_mix(hi[0], r);
+        w[3] = scale_pair_mix(hi[1], r);
         if (!row_ok) w[0] = w[1] = w[2] = w[3] = 0u;
         const half8_t b = __builtin_bit_cast(half8_t, make_uint4(w[0], w[1], w[2], w[3]));
         const int xcol = slot * kGroupCols + (4 * u + kk) * 8;
