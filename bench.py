@@ -50,7 +50,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="layer",
-                    choices=["layer", "sweep", "gemm", "prefill", "moe", "encode", "single", "all"])
+                    choices=["layer", "sweep", "gemm", "prefill", "moe", "encode", "decode",
+                             "single", "all"])
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", default="compiled", choices=["compiled", "eager"],
@@ -350,6 +351,7 @@ def cpu_baseline(layer, seconds):
 # ------------------------------------------------------------------------------------------------
 
 def bench_single_products(kind, steps, warmup):
+    import numpy as np
     import torch
     import workloads as W
     import bit_vector_quantized_amd as sage
@@ -371,6 +373,11 @@ def bench_single_products(kind, steps, warmup):
             for M in (1, 4, 16, 64):
                 c, X = W.small_batch(shape[0], shape[1], M)
                 cases.append((f"gemm_{shape[0]}x{shape[1]}_M{M}", c, X, M))
+                if M > 1:
+                    # compiled decoding: the rows arrive in stored order, the matrix runs with
+                    # pi = NULL and no reorder of X runs (SAGE paper §3.5)
+                    cases.append((f"gemm_{shape[0]}x{shape[1]}_M{M}_compiled", c,
+                                  np.ascontiguousarray(X[:, c.pi]), -M))
     if kind in ("prefill", "all"):
         for shape in ((9728, 2560), (2560, 9728)):
             for M in (128, 256, 512, 1024):
@@ -379,6 +386,10 @@ def bench_single_products(kind, steps, warmup):
     for name, c, x, M in cases:
         log(f"[case] {name}")
         base = upload_pack(c)
+        if M < 0:   # compiled decoding (see above)
+            M = -M
+            base = sage.Packed(base.d_out, base.d_in, base.log2K, base.V, base.packed,
+                               base.codebook, None)
         pb = packed_weight_bytes(base)
         copies = max(2, math.ceil(2 * MALL_BYTES / pb) + 1)
         ps = [base] + [clone_packed(base) for _ in range(copies - 1)]
@@ -424,6 +435,70 @@ def bench_single_products(kind, steps, warmup):
         del ps, base
         torch.cuda.empty_cache()
     return lines
+
+
+def bench_decode(layers=36, ctx=1024, warmup=5, measure=10):
+    """The synthetic end-to-end decode step (bit_vector_quantized_amd/decode_step.py): a
+    Qwen3-4B-shaped stack of 36 decoder layers on SAGE-packed synthetic weights, a 1024-token
+    context in the key/value caches, timed with the pages' protocol (SAGE paper App. A.2):
+    5 warmup steps, then 10 steps each timed with GPU events, median. The step launches every
+    kernel from Python (PyTorch attention around the libsage products), so it is also timed as
+    one HIP graph replay of the same step (same position, checked bit for bit against the eager
+    step) to separate the GPU time from the host's launch time."""
+    import torch
+    from bit_vector_quantized_amd import decode_step as ds
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20260)
+    log(f"[decode] building {layers} synthetic layers")
+    lws = [ds.random_layer(gen) for _ in range(layers)]
+    packed = sum(packed_weight_bytes(getattr(lw, n)) for lw in lws
+                 for n in ("q", "k", "v", "o", "gate", "up", "down"))
+    stack = ds.DecodeStack(lws, ctx=ctx, max_new=warmup + measure + 8, gen=gen)
+    h0 = (torch.randn(ds.QWEN3_4B.hidden, device="cuda", generator=gen) * 0.5).half()
+    times, h = ds.time_steps(stack, h0, warmup, measure)
+    eager_ms = ds.median(times)
+    # the same step as one graph (fixed position); checked against the eager step
+    pos = stack.pos
+    h_in = h.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        stack.pos = pos
+        stack.step(h_in)
+        graph = torch.cuda.CUDAGraph()
+        stack.pos = pos
+        with torch.cuda.graph(graph, stream=side):
+            h_graph = stack.step(h_in)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    stack.pos = pos
+    h_eager = stack.step(h_in)
+    graph_ok = True
+    gtimes = []
+    for i in range(warmup + measure):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        e1.synchronize()
+        graph_ok = graph_ok and bool(torch.equal(h_graph, h_eager))
+        if i >= warmup:
+            gtimes.append(e0.elapsed_time(e1))
+    graph_ms = ds.median(gtimes)
+    line = {"workload": f"decode_step_qwen3_4b_{layers}_layers_ctx{ctx}",
+            "protocol": f"{warmup} warmup steps, {measure} measured, median, GPU events",
+            "tpot_ms_eager": round(eager_ms, 4), "tokens_per_s_eager": round(1e3 / eager_ms, 1),
+            "tpot_ms_graph": round(graph_ms, 4) if graph_ok else None,
+            "tokens_per_s_graph": round(1e3 / graph_ms, 1) if graph_ok else None,
+            "graph_matches_eager": graph_ok,
+            "packed_bytes_per_step": packed,
+            "packed_gbs_graph": round(packed / (graph_ms * 1e-3) / 1e9, 1) if graph_ok else None,
+            "eager_ms_all": [round(t, 4) for t in times],
+            "finite": bool(torch.isfinite(h).all()),
+            "data": "synthetic (device-random fields, seeded)"}
+    print(json.dumps(line), flush=True)
+    return line
 
 
 def bench_encode(steps, warmup):
@@ -556,6 +631,8 @@ def main():
         bench_moe(args.steps, args.warmup)
     if args.workload in ("encode", "all"):
         bench_encode(args.steps, args.warmup)
+    if args.workload in ("decode", "all"):
+        bench_decode()
     if args.workload != "layer":
         return
 
