@@ -64,6 +64,7 @@ _SIGNATURES = {
     "sage_gemv_multi": (_I, [_PM, _PP, _PP, _I, _P, _SZ, _P]),
     "sage_gemm_small_workspace_bytes": (_I, [_PM, _I, _PSZ]),
     "sage_gemm_small": (_I, [_PM, _P, _I, _I, _P, _I, _P, _SZ, _P]),
+    "sage_gemm_small_noalloc": (_I, [_PM, _P, _I, _I, _P, _I, _P]),
     "sage_moe_gemv": (_I, [_PM, _I, _P, _I, _P, ctypes.c_int64, _P, ctypes.c_int64, _P]),
     "sage_moe_gemv_grouped": (_I, [_PM, _I, _I, _P, _I, _PP, _PI64, _PP, _PI64, _P]),
     "sage_stream_read": (_I, [_P, _SZ, _P, _P]),
@@ -411,6 +412,32 @@ def gemm_small(p: Packed, X, Y=None, ws=None, stream=None):
     _check("sage_gemm_small", lib().sage_gemm_small(ctypes.byref(d), _ptr(X), M, X.stride(0),
                                                     _ptr(Y), Y.stride(0), _ptr(ws), ws.numel(),
                                                     _stream(stream)))
+    return Y
+
+
+# Size of sage_gemm_small_noalloc's fixed device workspace (SAGE_NOALLOC_SCRATCH_BYTES in sage.h).
+NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024
+
+
+def gemm_small_noalloc(p: Packed, X, Y, stream=None):
+    """Y = X W_hat^T like gemm_small, through sage_gemm_small_noalloc: the library's fixed
+    per-device workspace instead of a caller's, so the call allocates no device memory (Y is the
+    caller's). Calls that overlap in time on one device race on that workspace."""
+    _check_packed(p)
+    _require_cuda(X)
+    _require_cuda(Y)
+    if X.dim() != 2 or str(X.dtype) != "torch.float16" or X.stride(1) != 1:
+        raise ValueError("X must be a 2-D float16 tensor with unit column stride")
+    M = X.shape[0]
+    if X.shape[1] < p.d_in:
+        raise ValueError(f"X rows hold {X.shape[1]} values, need d_in = {p.d_in}")
+    if (Y.dim() != 2 or str(Y.dtype) != "torch.float16" or Y.stride(1) != 1
+            or Y.shape[0] < M or Y.shape[1] < p.d_out):
+        raise ValueError("Y must be a float16 [M, >= d_out] tensor with unit column stride")
+    d = p.desc()
+    _check("sage_gemm_small_noalloc",
+           lib().sage_gemm_small_noalloc(ctypes.byref(d), _ptr(X), M, X.stride(0), _ptr(Y),
+                                         Y.stride(0), _stream(stream)))
     return Y
 
 

@@ -51,6 +51,7 @@ const char* sage_status_string(int status) {
     case SAGE_ERR_WORKSPACE: return "workspace missing or too small";
     case SAGE_ERR_HIP: return "HIP runtime error while queueing work";
     case SAGE_ERR_ARG: return "invalid argument";
+    case SAGE_ERR_SCRATCH: return "problem needs more workspace than the no-allocation entry point's fixed scratch (16 MiB)";
     default: return "unknown status";
   }
 }

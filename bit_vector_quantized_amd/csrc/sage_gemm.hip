@@ -16,6 +16,7 @@
 // tiles, the two column parts add their accumulators in LDS. All packed-weight loads of a wave are
 // issued up front through range-checked buffer loads, as in the batch-one kernel.
 #include <algorithm>
+#include <mutex>
 
 #include "sage_internal.hpp"
 
@@ -1030,34 +1031,59 @@ size_t workspace_for(const GemmArgs& A) {
 }  // namespace
 }  // namespace sage
 
-using namespace sage;
+namespace sage {
+namespace {
 
-extern "C" {
+// The no-allocation entry point's workspace: a fixed device array, one copy per device the library
+// runs on, held until the process ends. Host code never passes `scratch` itself (on the host the
+// name is a stand-in, not a device address): each device's address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kScratchBytes = size_t(SAGE_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
-int sage_gemm_small_workspace_bytes(const sage_matrix_t* m, int M, size_t* bytes) {
-  if (bytes == nullptr) return SAGE_ERR_NULL;
-  int st = check_matrix(m);
-  if (st != SAGE_OK) return st;
-  if (M < 1) return SAGE_ERR_SHAPE;
-  if (M == 1) return sage_gemv_workspace_bytes(m, bytes);  // one row: the batch-one kernel
-  GemmArgs A{};
-  A.d_out = m->d_out;
-  A.d_in = m->d_in;
-  A.M = M;
-  A.L = m->log2K;
-  plan(A, M);
-  *bytes = workspace_for(A);
+constexpr int kMaxDevices = 64;
+
+// Device address of the current device's scratch array (resolved on first use per device).
+int scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return SAGE_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return SAGE_ERR_ARG;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return SAGE_ERR_HIP;
+    }
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
   return SAGE_OK;
 }
 
-int sage_gemm_small(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, uint16_t* Y,
-                    int ldy, void* ws, size_t ws_bytes, sage_stream_t stream) {
+// Zero n words (the split-K arrival counters; a kernel, not hipMemsetAsync, so the call can be
+// captured into a graph).
+__global__ void __launch_bounds__(256) zero_words_kernel(uint32_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// Both small-batch entry points. With from_scratch the workspace is the device's scratch array
+// (ws and ws_bytes unused) and the arrival counters are zeroed before the product runs; otherwise
+// it is the caller's zero-ready workspace.
+int gemm_small_run(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, uint16_t* Y, int ldy,
+                   void* ws, size_t ws_bytes, bool from_scratch, sage_stream_t stream) {
   int st = check_matrix(m);
   if (st != SAGE_OK) return st;
   if (X == nullptr || Y == nullptr) return SAGE_ERR_NULL;
   if (M < 1 || ldx < m->d_in || ldy < m->d_out) return SAGE_ERR_SHAPE;
   if (!aligned(X, 4) || !aligned(Y, 2) || (ldx & 1)) return SAGE_ERR_ALIGN;
-  if (M == 1) return sage_gemv(m, X, Y, ws, ws_bytes, stream);
+  if (M == 1) return sage_gemv(m, X, Y, nullptr, 0, stream);  // no workspace
   GemmArgs A{};
   A.packed = static_cast<const uint8_t*>(m->packed);
   A.codebook = m->codebook;
@@ -1073,18 +1099,30 @@ int sage_gemm_small(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, u
   plan(A, M);
   const size_t need = workspace_for(A);
   const size_t xp_bytes = permuted_bytes(M, A.d_in);
-  if (need) {
+  if (from_scratch) {
+    if (need > kScratchBytes) return SAGE_ERR_SCRATCH;
+    if (need) {
+      st = scratch_address(&ws);
+      if (st != SAGE_OK) return st;
+    }
+  } else if (need) {
     if (ws == nullptr || ws_bytes < need) return SAGE_ERR_WORKSPACE;
     if (!aligned(ws, 256)) return SAGE_ERR_ALIGN;
   }
   char* wsb = static_cast<char*>(ws);
   const PfPlan pf = prefill_plan(A.L, A.d_out, A.d_in, M);
+  hipStream_t hs = (hipStream_t)stream;
   if (A.S > 1 && !pf.kq) {
     A.partial = reinterpret_cast<float*>(wsb + xp_bytes);
     A.counters = reinterpret_cast<uint32_t*>(
         wsb + xp_bytes + (size_t)A.mchunks * A.S * A.mrows_chunk * A.rt * kTileRows * 4);
+    if (from_scratch) {
+      // the array keeps whatever the device's previous call left there
+      const int n = A.mchunks * A.rpairs;
+      hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, hs,
+                         A.counters, n);
+    }
   }
-  hipStream_t hs = (hipStream_t)stream;
   // Activations already in stored column order (pi = NULL) with 16-byte aligned rows are read in
   // place (a producer that writes its output permuted saves the reorder launch).
   const bool direct = m->pi == nullptr && aligned(X, 16) && (ldx % 8) == 0;
@@ -1180,6 +1218,40 @@ int sage_gemm_small(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, u
     else launch(gemm_kernel<4, true, 2>, 7);
   }
   return hip_status();
+}
+
+
+}  // namespace
+}  // namespace sage
+
+using namespace sage;
+
+extern "C" {
+
+int sage_gemm_small_workspace_bytes(const sage_matrix_t* m, int M, size_t* bytes) {
+  if (bytes == nullptr) return SAGE_ERR_NULL;
+  int st = check_matrix(m);
+  if (st != SAGE_OK) return st;
+  if (M < 1) return SAGE_ERR_SHAPE;
+  if (M == 1) return sage_gemv_workspace_bytes(m, bytes);  // one row: the batch-one kernel
+  GemmArgs A{};
+  A.d_out = m->d_out;
+  A.d_in = m->d_in;
+  A.M = M;
+  A.L = m->log2K;
+  plan(A, M);
+  *bytes = workspace_for(A);
+  return SAGE_OK;
+}
+
+int sage_gemm_small(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, uint16_t* Y,
+                    int ldy, void* ws, size_t ws_bytes, sage_stream_t stream) {
+  return gemm_small_run(m, X, M, ldx, Y, ldy, ws, ws_bytes, false, stream);
+}
+
+int sage_gemm_small_noalloc(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, uint16_t* Y,
+                            int ldy, sage_stream_t stream) {
+  return gemm_small_run(m, X, M, ldx, Y, ldy, nullptr, 0, true, stream);
 }
 
 }  // extern "C"

@@ -28,7 +28,8 @@
  *     (idx >= K, an out-of-range permutation entry or expert id) are not checked on the device
  *     and give undefined results.
  *   - Thread safety: calls may be made from several host threads. Calls that overlap on the same
- *     stream run in order; concurrent calls that share an output or workspace buffer race.
+ *     stream run in order; concurrent calls that share an output or workspace buffer race (the
+ *     no-allocation entry point's fixed workspace is shared by all its calls on a device).
  */
 #ifndef SAGE_H
 #define SAGE_H
@@ -50,7 +51,9 @@ enum sage_status {
   SAGE_ERR_ALIGN = 4,     /* a pointer does not have the alignment stated for it */
   SAGE_ERR_WORKSPACE = 5, /* workspace pointer NULL or smaller than required */
   SAGE_ERR_HIP = 6,       /* the HIP runtime reported an error while queueing */
-  SAGE_ERR_ARG = 7        /* any other invalid argument (counts, strides, ids) */
+  SAGE_ERR_ARG = 7,       /* any other invalid argument (counts, strides, ids) */
+  SAGE_ERR_SCRATCH = 8    /* the problem needs more than the no-allocation entry point's fixed
+                             scratch (SAGE_NOALLOC_SCRATCH_BYTES) */
 };
 
 /* Human-readable text for a status code (static storage, never NULL). */
@@ -160,6 +163,27 @@ int sage_gemv_multi(const sage_matrix_t* mats, const uint16_t* const* xs, uint16
 int sage_gemm_small_workspace_bytes(const sage_matrix_t* m, int M, size_t* bytes);
 int sage_gemm_small(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, uint16_t* Y,
                     int ldy, void* ws, size_t ws_bytes, sage_stream_t stream);
+
+/*
+ * sage_gemm_small_noalloc: sage_gemm_small for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). Same product,
+ * arguments, kernels and results as sage_gemm_small, with no workspace argument: the workspace is
+ * a fixed array of SAGE_NOALLOC_SCRATCH_BYTES (16 MiB) in the library's device code, one copy per
+ * device, held from the library's first use on that device until the process ends. The call
+ * allocates nothing (no hipMalloc or hipFree, no allocating library routine); on its first use on
+ * a device it looks up that device's copy of the array.
+ *   Limit: problems whose sage_gemm_small_workspace_bytes() exceeds SAGE_NOALLOC_SCRATCH_BYTES
+ *   return SAGE_ERR_SCRATCH and queue nothing. Every Qwen3-4B-sized projection (d_out, d_in up
+ *   to 19456 x 2560 and 2560 x 9728) fits up to M = 64; prefill-sized M may not.
+ *   The array keeps the previous call's contents; each call zeroes what must start at zero (the
+ *   split-K arrival counters, by a kernel on `stream`) before its product.
+ *   All calls on one device share its array: calls that overlap in time on one device (other
+ *   streams, other host threads) race and give undefined results. Calls queued on one stream run
+ *   in order and are safe.
+ */
+#define SAGE_NOALLOC_SCRATCH_BYTES (16u * 1024u * 1024u)
+int sage_gemm_small_noalloc(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, uint16_t* Y,
+                            int ldy, sage_stream_t stream);
 
 /*
  * sage_moe_gemv: batch-one products of the routed experts of a mixture-of-experts layer in one

@@ -8,7 +8,7 @@ import pytest
 import bit_vector_quantized_amd as sage
 from bit_vector_quantized_amd import SageMatrix
 
-OK, NULL, SHAPE, SPLIT, ALIGN, WS, HIP, ARG = range(8)
+OK, NULL, SHAPE, SPLIT, ALIGN, WS, HIP, ARG, SCRATCH = range(9)
 
 
 @pytest.fixture(scope="module")
@@ -26,7 +26,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_status_strings(L):
-    for st in range(8):
+    for st in range(9):
         assert len(sage.status_string(st)) >= 2
     assert sage.status_string(99) == "unknown status"
 
@@ -98,6 +98,27 @@ def test_gemm_and_multi_validation(L):
     assert L.sage_gemv_multi(arr, xs, ys, 2, None, 0, None) == SPLIT
     assert L.sage_gemv_multi(arr, xs, ys, 0, None, 0, None) == ARG
     assert L.sage_gemv_multi(arr, xs, ys, 17, None, 0, None) == ARG
+
+
+def test_gemm_noalloc_validation(L):
+    """The no-allocation variant checks its arguments like sage_gemm_small and refuses, before
+    any device call, a problem whose workspace exceeds its fixed 16 MiB."""
+    X = ctypes.c_void_p(1 << 20)
+    Y = ctypes.c_void_p(1 << 21)
+    d = _desc()
+    assert sage.NOALLOC_SCRATCH_BYTES == 16 << 20
+    assert L.sage_gemm_small_noalloc(None, X, 4, 256, Y, 64, None) == NULL
+    assert L.sage_gemm_small_noalloc(ctypes.byref(d), None, 4, 256, Y, 64, None) == NULL
+    assert L.sage_gemm_small_noalloc(ctypes.byref(d), X, 0, 256, Y, 64, None) == SHAPE
+    assert L.sage_gemm_small_noalloc(ctypes.byref(d), X, 4, 257, Y, 64, None) == ALIGN
+    assert L.sage_gemm_small_noalloc(ctypes.byref(_desc(log2K=9, V=1)), X, 4, 256, Y, 64,
+                                     None) == SPLIT
+    big = _desc(d_out=2560, d_in=9728)
+    n = ctypes.c_size_t(0)
+    assert L.sage_gemm_small_workspace_bytes(ctypes.byref(big), 128, ctypes.byref(n)) == OK
+    assert n.value > sage.NOALLOC_SCRATCH_BYTES
+    assert L.sage_gemm_small_noalloc(ctypes.byref(big), X, 128, 9728, Y, 2560, None) == SCRATCH
+    assert "16 MiB" in sage.status_string(SCRATCH)
 
 
 def test_moe_validation(L):
