@@ -10,7 +10,7 @@ One layer, for one new token at position n:
     a = RMSNorm(h) written in q/k/v's stored order          (sage_rmsnorm_permute)
     q, k, v = W_q a, W_k a, W_v a                          (one sage_gemv_multi launch)
     q, k = per-head RMSNorm (Qwen3's q/k norms), rotary position n (PyTorch)
-    K[:, n], V[:, n] = k, v;  o = SDPA(q, K[:, :n+1], V[:, :n+1]) (PyTorch, grouped-query, fp32)
+    K[:, n], V[:, n] = k, v;  o = SDPA(q, K[:, :n+1], V[:, :n+1]) (PyTorch, grouped-query, fp16)
     h = h + W_o o                                            (sage_gemv: o arrives in original
                                                               order, the product gathers it)
     b = RMSNorm(h) written in gate/up's stored order         (sage_rmsnorm_permute)
@@ -18,8 +18,9 @@ One layer, for one new token at position n:
     m = silu(g) * u written in down's stored order           (sage_silu_mul_permute)
     h = h + W_down m                                         (sage_gemv)
 
-The token embedding, the final norm and the LM head lie outside the stack. The key/value caches
-hold the context in fp32 (attention runs in fp32 and rounds its output to fp16 once).
+The token embedding, the final norm and the LM head lie outside the stack. Activations and the
+key/value caches are fp16, as in the paper's end-to-end runs (§4.4: FP16 activations and KV cache);
+the per-head norms and the rotation are computed in fp32 and rounded to fp16 once.
 """
 from __future__ import annotations
 
@@ -128,14 +129,18 @@ class DecodeStack:
         n = ctx + max_new
         self.max_len = n
         shape = (len(layers), dims.kv_heads, n, dims.head_dim)
-        self.kcache = torch.zeros(shape, dtype=torch.float32, device="cuda")
-        self.vcache = torch.zeros(shape, dtype=torch.float32, device="cuda")
+        self.kcache = torch.zeros(shape, dtype=torch.float16, device="cuda")
+        self.vcache = torch.zeros(shape, dtype=torch.float16, device="cuda")
         if ctx > 0:
             self.kcache[:, :, :ctx].normal_(generator=gen)
             self.vcache[:, :, :ctx].normal_(generator=gen)
+        # rotary tables for every position the caches can hold, [n, head_dim / 2] each
         half = dims.head_dim // 2
-        self.inv_freq = 1.0 / (dims.rope_theta ** (
-            torch.arange(0, half, dtype=torch.float32, device="cuda") / half))
+        inv_freq = 1.0 / (dims.rope_theta ** (
+            torch.arange(0, half, dtype=torch.float64, device="cuda") / half))
+        ang = torch.arange(n, dtype=torch.float64, device="cuda")[:, None] * inv_freq[None, :]
+        self.cos = torch.cos(ang).float()
+        self.sin = torch.sin(ang).float()
 
     # -- the linear chains (libsage kernels) --------------------------------------------------
     def attn_in(self, lw: LayerWeights, h):
@@ -160,8 +165,7 @@ class DecodeStack:
 
     def _rope(self, t, pos: int):
         import torch
-        ang = pos * self.inv_freq
-        cos, sin = torch.cos(ang), torch.sin(ang)
+        cos, sin = self.cos[pos], self.sin[pos]
         t1, t2 = t[..., : t.shape[-1] // 2], t[..., t.shape[-1] // 2:]
         return torch.cat((t1 * cos - t2 * sin, t2 * cos + t1 * sin), dim=-1)
 
@@ -170,15 +174,15 @@ class DecodeStack:
         import torch
         import torch.nn.functional as F
         d = self.dims
-        qh = self._rope(self._head_norm(q.view(d.heads, d.head_dim), lw.q_norm), self.pos)
+        qh = self._rope(self._head_norm(q.view(d.heads, d.head_dim), lw.q_norm), self.pos).half()
         kh = self._rope(self._head_norm(k.view(d.kv_heads, d.head_dim), lw.k_norm), self.pos)
-        self.kcache[li, :, self.pos] = kh
-        self.vcache[li, :, self.pos] = v.view(d.kv_heads, d.head_dim).float()
+        self.kcache[li, :, self.pos] = kh.half()
+        self.vcache[li, :, self.pos] = v.view(d.kv_heads, d.head_dim)
         n = self.pos + 1
         o = F.scaled_dot_product_attention(
             qh[None, :, None, :], self.kcache[li, None, :, :n], self.vcache[li, None, :, :n],
             enable_gqa=True)
-        return o.reshape(d.heads * d.head_dim).half()
+        return o.reshape(d.heads * d.head_dim)
 
     def layer(self, li: int, h):
         lw = self.layers[li]
