@@ -67,14 +67,6 @@ __device__ inline __amdgpu_buffer_rsrc_t view(const void* base, uint32_t bytes) 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
 
-// Sign masks of one nibble (n < 16): bits 0/1 -> sign bits 15/31 of the first fp16 pair, bits 2/3
-// -> sign bits 15/31 of the second pair. Two shifted copies of n OR-ed and masked put each bit in
-// place (three ALU operations a dword; measured faster than a 16-entry LDS table, which costs a
-// load a nibble against the LDS wait counter).
-__device__ inline uint2 sign_masks(uint32_t n) {
-  return make_uint2(((n << 15) | (n << 30)) & 0x80008000u, ((n << 13) | (n << 28)) & 0x80008000u);
-}
-
 // X[:, pi] for M rows into a dense [M][d_in] buffer (the reorder the paper does once per
 // projection before prefill, §3.5). A workgroup copies kR whole rows of X into LDS (all its
 // 16-byte loads issued before any is stored), then each thread gathers 8 consecutive outputs of
@@ -197,16 +189,6 @@ __global__ void __launch_bounds__(256) permute_gather_kernel(const uint16_t* __r
   const int src = pi ? (int)min((uint32_t)pi[p], (uint32_t)d_in - 1u) : p;
   for (int m = blockIdx.y; m < M; m += gridDim.y)
     Xp[(int64_t)m * d_in + p] = X[(int64_t)m * ldx + src];
-}
-
-// fp16(r * c) for the two fp16 values of a dword: each weight is the fp32 product rounded once to
-// fp16, as the paper's prefill kernel decodes r_hat (s (.) c_z) in FP32 and then stores FP16 (App.
-// A.1).
-__device__ inline uint32_t scale_pair(uint32_t c, float r) {
-  const half2_t h = __builtin_bit_cast(half2_t, c);
-  const _Float16 lo = (_Float16)((float)h[0] * r);
-  const _Float16 hi = (_Float16)((float)h[1] * r);
-  return __builtin_bit_cast(uint32_t, half2_t{lo, hi});
 }
 
 // One fp16 pair c scaled by r: each half becomes fp16(c_i * r) with a single rounding of the exact
@@ -563,7 +545,7 @@ struct PrefillArgs {
 };
 
 __host__ __device__ inline uint32_t prefill_slab_offset(int L) {
-  return (1u << L) * 256u + 256u;  // after the codebook replicas and 256 spare bytes
+  return (1u << L) * 256u + 256u;  // after the sign-applied codeword table and 256 spare bytes
 }
 
 // One lane's packed words of one row in one group: payload dwords P0..P7, then X and G.
@@ -572,38 +554,42 @@ struct RowWords {
   u32x2 side;
 };
 
-// First half of a subvector decode: the codeword replica, the two sign masks and the radius.
-// The codeword's LDS read is only issued here; decode_finish consumes it a pipeline step later.
+// First half of a subvector decode: the two sign-applied codeword halves and the radius. The
+// table reads are only issued here; decode_finish consumes them a pipeline step later.
 struct Fetched {
-  uint4 c;
-  uint2 mlo, mhi;
+  u32x2 lo, hi;
   float r;
 };
 
+// Lanes of the first half-wave (rot = 0, hb = 0) take subvector a = 2s of pair s, the others
+// (rot = 14, hb = 1) subvector b = 2s + 1, whose index, low sign nibble and radius code the
+// rotation by 14 brings to a's positions. The table keys come straight from the packed word as in
+// the batch-one kernel: the low sign nibble sits next to z, the high one is rotated into place
+// from X (a) or from P (b).
 template <int L>
-__device__ __forceinline__ Fetched decode_fetch(const RowWords& w, int s, int h, const uint8_t* cb,
-                                                uint32_t laneoff) {
-  constexpr uint32_t kK = 1u << L;
+__device__ __forceinline__ Fetched decode_fetch(const RowWords& w, int s, uint32_t rot, uint32_t hb,
+                                                const uint8_t* cb) {
+  using TK = TKeys<L>;
   constexpr uint32_t kV = (1u << (10 - L)) - 1u;
   const uint32_t P = s < 4 ? w.a[s & 3] : w.b[s & 3];
   const uint32_t X = w.side[0], G = w.side[1];
-  // subvector 2s + h of the group: pair s, half a (h = 0) or b (h = 1)
-  const uint32_t z = h ? ((P >> 17) & (kK - 1u)) : ((P >> 3) & (kK - 1u));
-  const uint32_t q = h ? ((P >> (21 + L)) & kV) : ((P >> (7 + L)) & kV);
-  const uint32_t lo = h ? ((P >> (17 + L)) & 15u) : ((P >> (3 + L)) & 15u);
-  const uint32_t hi = h ? ((P >> 31) | ((P & 7u) << 1)) : ((X >> (4 * s)) & 15u);
+  const uint32_t Pr = rotr32(P, rot);
+  const uint32_t klo = Pr & TK::kKeyMask;
+  const uint32_t src = hb ? P : X;
+  const uint32_t sh = hb ? (uint32_t)(28 - L) : ((4u * (uint32_t)s + 29u - (uint32_t)L) & 31u);
+  const uint32_t khi = (rotr32(src, sh) & TK::kSignMask) | (klo & ~TK::kSignMask);
+  const uint32_t q = (Pr >> (7 + L)) & kV;
   Fetched o;
   o.r = fmaf((float)q, h2f(G >> 16), h2f(G));
-  o.c = *reinterpret_cast<const uint4*>(cb + z * 256 + laneoff);
-  o.mlo = sign_masks(lo);
-  o.mhi = sign_masks(hi);
+  o.lo = *reinterpret_cast<const u32x2*>(cb + klo);
+  o.hi = *reinterpret_cast<const u32x2*>(cb + TK::kTHi + khi);
   return o;
 }
 
 __device__ __forceinline__ half8_t decode_finish(const Fetched& d) {
   return __builtin_bit_cast(
-      half8_t, make_uint4(scale_pair(d.c.x ^ d.mlo.x, d.r), scale_pair(d.c.y ^ d.mlo.y, d.r),
-                          scale_pair(d.c.z ^ d.mhi.x, d.r), scale_pair(d.c.w ^ d.mhi.y, d.r)));
+      half8_t, make_uint4(scale_pair_mix(d.lo[0], d.r), scale_pair_mix(d.lo[1], d.r),
+                          scale_pair_mix(d.hi[0], d.r), scale_pair_mix(d.hi[1], d.r)));
 }
 
 template <int L, int kQ>
@@ -692,9 +678,18 @@ __device__ void prefill_body(const PrefillArgs& A, uint8_t* smem) {
   SAGE_PF_X(0)
   SAGE_PF_WORDS(0, 0)
   SAGE_PF_WORDS(1, 1)
+  // the sign-applied codeword table: thread z < K writes the 32 halves of codeword z
   if (tid < (int)kK) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) *reinterpret_cast<u32x4*>(cb + tid * 256 + r * 16) = cw;
+    for (int hs = 0; hs < 32; ++hs) {
+      const uint32_t hh = (uint32_t)hs >> 4, sg = (uint32_t)hs & 15u;
+      const uint32_t c01 = hh ? cw[2] : cw[0];
+      const uint32_t c23 = hh ? cw[3] : cw[1];
+      const uint32_t m01 = ((sg & 1u) << 15) | ((sg & 2u) << 30);
+      const uint32_t m23 = ((sg & 4u) << 13) | ((sg & 8u) << 28);
+      *reinterpret_cast<u32x2*>(cb + ((uint32_t)hs * kK + (uint32_t)tid) * 8u) =
+          u32x2{c01 ^ m01, c23 ^ m23};
+    }
   }
   // the first slab has landed once only the two word groups are outstanding
   asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
@@ -707,10 +702,11 @@ __device__ void prefill_body(const PrefillArgs& A, uint8_t* smem) {
     for (int q = 0; q < kQ; ++q)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[t][q][v] = 0.0f;
-  const uint32_t laneoff = (uint32_t)(lane & 15) * 16u;
+  const uint32_t rot = h ? 14u : 0u;
+  const uint32_t hb = (uint32_t)h;
 
   // One group, software-pipelined over its 8 steps: while the MFMAs of step s run, the operand
-  // loads of step s + 1 and the codebook/mask loads of step s + 2 are in flight and step s + 1's
+  // loads of step s + 1 and the table reads of step s + 2 are in flight and step s + 1's
   // decode finishes on the vector ALU. Activations of g + 1 go to the other slab buffer and the
   // words of g + 2 into ring slot (k + 2) % 3 at the start; at the end every wave waits for its
   // slab loads (all but the 6 word loads just issued) and meets the others at the barrier.
@@ -724,8 +720,8 @@ __device__ void prefill_body(const PrefillArgs& A, uint8_t* smem) {
     half8_t bv[2][2];                                                                         \
     half8_t av[2][kQ];                                                                        \
     _Pragma("unroll") for (int t = 0; t < 2; ++t) {                                           \
-      fd[0][t] = decode_fetch<L>(wr[k][t], 0, h, cb, laneoff);                                \
-      fd[1][t] = decode_fetch<L>(wr[k][t], 1, h, cb, laneoff);                                \
+      fd[0][t] = decode_fetch<L>(wr[k][t], 0, rot, hb, cb);                                \
+      fd[1][t] = decode_fetch<L>(wr[k][t], 1, rot, hb, cb);                                \
     }                                                                                         \
     _Pragma("unroll") for (int q = 0; q < kQ; ++q)                                            \
       av[0][q] = *reinterpret_cast<const half8_t*>(abuf + q * 8192 + (a_hm ^ 0u));            \
@@ -739,7 +735,7 @@ __device__ void prefill_body(const PrefillArgs& A, uint8_t* smem) {
       }                                                                                       \
       if (s + 2 < 8) {                                                                        \
         _Pragma("unroll") for (int t = 0; t < 2; ++t)                                         \
-          fd[s & 1][t] = decode_fetch<L>(wr[k][t], s + 2, h, cb, laneoff);                    \
+          fd[s & 1][t] = decode_fetch<L>(wr[k][t], s + 2, rot, hb, cb);                    \
       }                                                                                       \
       _Pragma("unroll") for (int q = 0; q < kQ; ++q)                                          \
         _Pragma("unroll") for (int t = 0; t < 2; ++t)                                         \
