@@ -61,6 +61,7 @@ struct GemmArgs {
   int32_t mrows_chunk;  // activation rows per workgroup = 16 * NT
   int32_t vec_x;        // X rows are 16-byte aligned and already in permuted order (kVec)
   int32_t tiles;        // workgroup shape (GShape<tiles>)
+  int32_t stream;       // activations streamed through LDS a group at a time (1 x 4 shape)
 };
 
 __device__ inline __amdgpu_buffer_rsrc_t view(const void* base, uint32_t bytes) {
@@ -217,9 +218,16 @@ __device__ inline uint32_t rotr32(uint32_t v, uint32_t n) { return __builtin_amd
 // LDS layout: the sign-applied codeword table [256 K bytes], 128 spare bytes, flag, then the X tile
 // [NT*16][gs*128 + 8] fp16 (also the part-sum exchange once the products are done).
 __host__ __device__ inline uint32_t gemm_xs_offset(int L) { return (1u << L) * 256u + 144u; }
+// Streamed activations: two buffers of four 16 NT-row slabs (one per column part), each row one
+// group's 128 channels (256 bytes, 16-byte chunk c of row R at slot c ^ (R % 16)), after the table.
+__host__ __device__ inline uint32_t stream_xs_offset(int L) { return (1u << L) * 256u + 256u; }
+__host__ __device__ inline uint32_t stream_lds(int L, int nt) {
+  return stream_xs_offset(L) + 2u * 4u * (uint32_t)nt * 16u * 256u;
+}
 
-template <int L, int NT, bool kVec, int kGT>
+template <int L, int NT, bool kVec, int kGT, bool kStream>
 __device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint8_t* smem) {
+  static_assert(!kStream || (kVec && kGT == 1), "streamed activations need the 1 x 4 shape");
   constexpr uint32_t kK = 1u << L;
   constexpr int kGTiles = GShape<kGT>::kTiles;
   constexpr int kGParts = GShape<kGT>::kParts;
@@ -248,7 +256,7 @@ __device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint
 
   uint8_t* cb = smem;
   uint32_t* flag = reinterpret_cast<uint32_t*>(smem + kK * 256 + 128);
-  _Float16* xs = reinterpret_cast<_Float16*>(smem + gemm_xs_offset(L));
+  _Float16* xs = reinterpret_cast<_Float16*>(smem + (kStream ? stream_xs_offset(L) : gemm_xs_offset(L)));
 
   // 1. Loads: codebook, pi, activations, then every packed group of the wave.
   const __amdgpu_buffer_rsrc_t cb_rs = view(A.codebook, kK * 16u);
@@ -272,7 +280,37 @@ __device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint
     for (int q = 0; q < kCpt; ++q)
       pv[q] = __builtin_amdgcn_raw_buffer_load_b32(pi_rs, (tid + q * kGThreads) * 4, 0, 0);
   }
-  if constexpr (kVec) {
+  // Streamed: iteration it needs group k0 + it of every column part. Its activations are 4 slabs
+  // of 16 NT rows x 256 bytes = 16 NT pieces of 1 KiB (4 rows each); wave w loads pieces w, w + 16,
+  // ... straight into LDS. Lane l of a piece fills row r0 + l / 16, slot l % 16, i.e. chunk
+  // (l % 16) ^ (row % 16) of the row. Groups past a part's range read zeros.
+  constexpr int kSlabRows = NT * 16;
+  const int gpp_s = (ngl + 3) / 4;
+  auto stage = [&](int it) {
+    if constexpr (kStream) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int piece = wave + 16 * t;
+        const int pp_ = piece / (kSlabRows / 4);
+        const int r0 = (piece % (kSlabRows / 4)) * 4;
+        const int row = r0 + (lane >> 4);
+        const int chunk = (lane & 15) ^ (row & 15);
+        const int gi = pp_ * gpp_s + it;
+        const bool ok = it < gpp_s && gi < ngl;
+        const uint32_t off =
+            ok ? (uint32_t)(((int64_t)row * A.ldx + c0 + gi * kGroupCols + chunk * 8) * 2)
+               : kNowhere;
+        uint8_t* dst = reinterpret_cast<uint8_t*>(xs) +
+                       ((uint32_t)(((it & 1) * 4 + pp_) * kSlabRows + r0) * 256u);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rs, (__attribute__((address_space(3))) void*)dst,
+                                                 16, off, 0, 0, 0);
+      }
+    }
+  };
+  if constexpr (kStream) {
+    stage(0);
+    stage(1);
+  } else if constexpr (kVec) {
 #pragma unroll
     for (int i = 0; i < kVecLoads; ++i) {
       const int e = tid + i * kGThreads;
@@ -322,7 +360,9 @@ __device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint
           u32x2{c01 ^ m01, c23 ^ m23};
     }
   }
-  if constexpr (kVec) {
+  if constexpr (kStream) {
+    // nothing: the activations go straight to LDS
+  } else if constexpr (kVec) {
 #pragma unroll
     for (int i = 0; i < kVecLoads; ++i) {
       const int e = tid + i * kGThreads;
@@ -341,13 +381,76 @@ __device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint
       }
     }
   }
-  __syncthreads();
+  // (streamed: the first iteration's barrier covers the table)
+  if constexpr (!kStream) __syncthreads();
 
   // 3. Decode once, multiply NT times.
   float4_t acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
   const bool row_ok = tile_ok && wrow < A.d_out;  // padded rows decode to zero weights anyway
+  if constexpr (kStream) {
+    // Iteration it: every wave waits for its own activation loads of the iteration (the counts are
+    // the loads issued after them: iteration 1's loads and the 2 kGMaxUnits packed-word loads
+    // before iteration 0, the packed-word loads before iteration 1, none later) and meets the
+    // others at the barrier, after which the other buffer is free for iteration it + 1.
+#pragma unroll
+    for (int it = 0; it < kGMaxUnits; ++it) {
+      if (it < gpp_s) {
+        if (it == 0)
+          asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NT + 2 * kGMaxUnits)
+                       : "memory");
+        else if (it == 1)
+          asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * kGMaxUnits)
+                       : "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (it >= 1 && it + 1 < gpp_s) stage(it + 1);
+        if (it < ngp) {
+          const uint8_t* abase = reinterpret_cast<const uint8_t*>(xs) +
+                                 (uint32_t)(((it & 1) * 4 + part) * kSlabRows) * 256u;
+          const float mu = h2f(sd[it][1]);
+          const float dl = h2f(sd[it][1] >> 16);
+          using TK = TKeys<L>;
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            const uint32_t P = (kk < 2) ? pp[it][0] : pp[it][1];
+            const uint32_t pair = 2u * (uint32_t)u + (uint32_t)(kk >> 1);
+            uint32_t klo, khi, q;
+            if ((kk & 1) == 0) {
+              klo = P & TK::kKeyMask;
+              khi = (rotr32(sd[it][0], (4u * pair + 29u - (uint32_t)L) & 31u) & TK::kSignMask) |
+                    (klo & ~TK::kSignMask);
+              q = (P >> (7 + L)) & ((1u << (10 - L)) - 1u);
+            } else {
+              const uint32_t R = rotr32(P, 14);
+              klo = R & TK::kKeyMask;
+              khi = (rotr32(P, 28 - L) & TK::kSignMask) | (klo & ~TK::kSignMask);
+              q = (R >> (7 + L)) & ((1u << (10 - L)) - 1u);
+            }
+            const float r = fmaf((float)q, dl, mu);
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(cb + klo);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(cb + TK::kTHi + khi);
+            uint32_t w[4];
+            w[0] = scale_pair_mix(lo[0], r);
+            w[1] = scale_pair_mix(lo[1], r);
+            w[2] = scale_pair_mix(hi[0], r);
+            w[3] = scale_pair_mix(hi[1], r);
+            if (!row_ok) w[0] = w[1] = w[2] = w[3] = 0u;
+            const half8_t b = __builtin_bit_cast(half8_t, make_uint4(w[0], w[1], w[2], w[3]));
+            // activation row t * 16 + j, chunk 4 u + kk of the group, at slot chunk ^ j
+            const uint32_t aoff = (uint32_t)j * 256u + (uint32_t)(((4 * u + kk) ^ j) * 16);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+              const half8_t a =
+                  *reinterpret_cast<const half8_t*>(abase + (uint32_t)t * 4096u + aoff);
+              acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[t], 0, 0, 0);
+            }
+          }
+        }
+      }
+    }
+  } else {
   // the SIMD's issue slots go to the oldest wave first; a wave's priority is its remaining groups
   // (3 down to 0), so the four waves of a SIMD advance together instead of one after another
   __builtin_amdgcn_s_setprio(3);
@@ -402,6 +505,7 @@ __device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint
   }
 
   __builtin_amdgcn_s_setprio(0);
+  }
   // 4. The other column parts hand their sums to the first through LDS (the X tile is done);
   // part order is kept.
   __syncthreads();
@@ -490,7 +594,7 @@ __device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint
   if (tid == 0) counter_reset(counter);
 }
 
-template <int NT, bool kVec, int kGT>
+template <int NT, bool kVec, int kGT, bool kStream = false>
 __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs A) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int per_chunk = A.rpairs * A.S;
@@ -499,11 +603,11 @@ __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs A) {
   const int rp = local / A.S;
   const int split = local - rp * A.S;
   switch (A.L) {
-    case 4: gemm_body<4, NT, kVec, kGT>(A, rp, split, mchunk, smem); break;
-    case 5: gemm_body<5, NT, kVec, kGT>(A, rp, split, mchunk, smem); break;
-    case 6: gemm_body<6, NT, kVec, kGT>(A, rp, split, mchunk, smem); break;
-    case 7: gemm_body<7, NT, kVec, kGT>(A, rp, split, mchunk, smem); break;
-    default: gemm_body<8, NT, kVec, kGT>(A, rp, split, mchunk, smem); break;
+    case 4: gemm_body<4, NT, kVec, kGT, kStream>(A, rp, split, mchunk, smem); break;
+    case 5: gemm_body<5, NT, kVec, kGT, kStream>(A, rp, split, mchunk, smem); break;
+    case 6: gemm_body<6, NT, kVec, kGT, kStream>(A, rp, split, mchunk, smem); break;
+    case 7: gemm_body<7, NT, kVec, kGT, kStream>(A, rp, split, mchunk, smem); break;
+    default: gemm_body<8, NT, kVec, kGT, kStream>(A, rp, split, mchunk, smem); break;
   }
 }
 
@@ -990,6 +1094,23 @@ void plan(GemmArgs& A, int M) {
   A.mchunks = ceil_div(M, A.mrows_chunk);
   const int nt = tiles_for(M);
   const int64_t cus = device_cu_count();
+  A.stream = 0;
+  // 17 or more rows (X always in stored order from 8 rows on): one 64-row tile x 4 column parts
+  // with the activations streamed through LDS a group at a time, so a workgroup can take every
+  // column group (at most 20) of its tile; splits only where the row tiles alone leave most compute
+  // units idle, at least one group per part
+  if (nt >= 2 && M >= kPermuteMinRows && stream_lds(A.L, nt) <= kLdsLimit) {
+    A.stream = 1;
+    A.tiles = 1;
+    A.rpairs = A.rt;
+    const int64_t tiles = (int64_t)A.mchunks * A.rt;
+    int64_t S = std::max<int64_t>(1, cus / tiles);
+    S = std::max<int64_t>(S, ceil_div(A.ng, gshape_max_gs(1)));
+    S = std::min<int64_t>(S, std::max(1, A.ng / 4));
+    A.gs = ceil_div(A.ng, (int)S);
+    A.S = ceil_div(A.ng, A.gs);
+    return;
+  }
   if (nt == 1 && M >= kPermuteMinRows && A.ng <= gshape_max_gs(1) && (int64_t)A.mchunks * A.rt <= cus &&
       lds_for(A.L, nt, A.ng, 1) <= kLdsLimit) {
     A.tiles = 1;
@@ -1193,7 +1314,7 @@ int gemm_small_run(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, ui
     A.vec_x = 0;  // fewer than kPermuteMinRows rows, gathered through pi by the kernel
   }
   const int nt = tiles_for(M);
-  const size_t lds = lds_for(A.L, nt, A.gs, A.tiles);
+  const size_t lds = A.stream ? stream_lds(A.L, nt) : lds_for(A.L, nt, A.gs, A.tiles);
   const unsigned grid = (unsigned)(A.mchunks * A.rpairs * A.S);
   // Each instantiation gets its LDS limit raised once (slot = shape * 4 + variant).
   static bool attr_set[8] = {};
@@ -1205,7 +1326,10 @@ int gemm_small_run(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, ui
     }
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kGThreads), lds, hs, A);
   };
-  if (A.tiles == 1) {  // nt == 1, whole-vector rows
+  if (A.stream) {  // nt == 2 or 4, 1 x 4 with streamed activations
+    if (nt == 2) launch(gemm_kernel<2, true, 1, true>, 2);
+    else launch(gemm_kernel<4, true, 1, true>, 3);
+  } else if (A.tiles == 1) {  // nt == 1, whole-vector rows
     launch(gemm_kernel<1, true, 1>, 1);
   } else {
     if (!A.vec_x) launch(gemm_kernel<1, false, 2>, 4);  // fewer than kPermuteMinRows rows: nt == 1

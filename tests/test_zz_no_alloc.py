@@ -61,7 +61,8 @@ def _same(name, Y_noalloc, Y_ws):
 
 
 @pytest.mark.parametrize("shape,M1,M2", [
-    ((9728, 2560), 64, 24),    # split-K small-batch kernel, then a smaller split-K plan
+    ((4096, 2560), 64, 24),    # split-K small-batch kernel, then a smaller split-K plan
+    ((9728, 2560), 64, 17),    # every column group in one workgroup (no split-K), twice
     ((2560, 9728), 48, 17),    # gathered through pi in the workspace, split-K
     ((1024, 2560), 96, 8),     # a prefill-kernel plan, then one 1 x 4 split
 ])
