@@ -490,6 +490,25 @@ def test_gemm_small_workgroup_shapes(M, d_in):
     check_gemm(f"70x{d_in} M={M}", c, X, Y)
 
 
+@pytest.mark.parametrize("d_out,d_in,M", [
+    (70, 128, 17),      # one column group: parts 1-3 idle, ragged last row tile
+    (130, 256, 32),     # two groups, two row tiles
+    (64, 384, 48),      # three groups over four parts
+    (4160, 640, 100),   # five groups (two iterations, a part with one), two activation chunks
+    (70, 2688, 33),     # 21 groups: split over the columns in the streamed plan
+    (300, 2560, 64),    # 20 groups, five iterations per part, split-K on few row tiles
+])
+def test_gemm_streamed_activation_shapes(d_out, d_in, M):
+    """From 17 rows the activations stream through LDS one column group per part and iteration:
+    ragged group counts (some parts without groups), one or several iterations, one or two
+    activation chunks, with and without split-K."""
+    rng = W.rng_for(147, d_out, d_in, M)
+    c = W.draw_codes(rng, d_out, d_in, 64, 4)
+    X = W.draw_x(rng, (M, d_in))
+    Y = sage.gemm_small(upload_pack(c), _dev(X))
+    check_gemm(f"{d_out}x{d_in} M={M} streamed", c, X, Y)
+
+
 @pytest.mark.parametrize("M", [1, 4, 16, 64])
 @pytest.mark.parametrize("shape", [(9728, 2560), (2560, 9728)])
 def test_gemm_small_full_size(shape, M):
