@@ -10,7 +10,8 @@ One layer, for one new token at position n:
     a = RMSNorm(h) written in q/k/v's stored order          (sage_rmsnorm_permute)
     q, k, v = W_q a, W_k a, W_v a                          (one sage_gemv_multi launch)
     q, k = per-head RMSNorm (Qwen3's q/k norms), rotary position n (PyTorch)
-    K[:, n], V[:, n] = k, v;  o = SDPA(q, K[:, :n+1], V[:, :n+1]) (PyTorch, grouped-query, fp16)
+    K[:, n], V[:, n] = k, v;  o = softmax(q K[:, :n+1]^T / sqrt(128)) V[:, :n+1]
+                                                             (PyTorch, grouped-query, fp16 products)
     h = h + W_o o                                            (sage_gemv: o arrives in original
                                                               order, the product gathers it)
     b = RMSNorm(h) written in gate/up's stored order         (sage_rmsnorm_permute)
@@ -160,8 +161,8 @@ class DecodeStack:
 
     # -- attention (PyTorch) --------------------------------------------------------------------
     def _head_norm(self, t, w):
-        t32 = t.float()
-        return t32 * torch_rsqrt_mean(t32, self.dims.eps) * w.float()
+        import torch.nn.functional as F
+        return F.rms_norm(t.float(), (self.dims.head_dim,), w.float(), self.dims.eps)
 
     def _rope(self, t, pos: int):
         import torch
@@ -179,9 +180,14 @@ class DecodeStack:
         self.kcache[li, :, self.pos] = kh.half()
         self.vcache[li, :, self.pos] = v.view(d.kv_heads, d.head_dim)
         n = self.pos + 1
-        o = F.scaled_dot_product_attention(
-            qh[None, :, None, :], self.kcache[li, None, :, :n], self.vcache[li, None, :, :n],
-            enable_gqa=True)
+        # grouped-query attention for one query as two batched fp16 products: the 4 query heads of
+        # a key/value head form the columns of one operand (a contiguous [kv_heads, head_dim, 4]),
+        # the cached keys and values are read in place
+        g = d.heads // d.kv_heads
+        qg = qh.view(d.kv_heads, g, d.head_dim).transpose(1, 2).contiguous()
+        s = torch.matmul(self.kcache[li, :, :n], qg).float() * (d.head_dim ** -0.5)
+        pr = torch.softmax(s, dim=1).half()                         # [kv_heads, n, g]
+        o = torch.matmul(pr.transpose(1, 2).contiguous(), self.vcache[li, :, :n])
         return o.reshape(d.heads * d.head_dim)
 
     def layer(self, li: int, h):
@@ -200,11 +206,6 @@ class DecodeStack:
             h = self.layer(li, h)
         self.pos += 1
         return h
-
-
-def torch_rsqrt_mean(t32, eps: float):
-    import torch
-    return torch.rsqrt((t32 * t32).mean(dim=-1, keepdim=True) + eps)
 
 
 def time_steps(stack: DecodeStack, h0, warmup: int = 5, measure: int = 10):
