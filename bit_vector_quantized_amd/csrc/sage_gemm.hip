@@ -10,10 +10,12 @@
 // the channel order inside the 32-wide contraction is the same for A and B. One decoded subvector
 // feeds NT = 1, 2 or 4 MFMAs (16, 32 or 64 activation rows).
 //
-// Workgroup: 16 wavefronts = 2 weight tiles of 64 rows (4 waves of 16 rows each) x 2 column parts.
-// It owns a range of column groups (split-K over workgroups) and one chunk of activation rows; the
-// activations of its columns are staged once in LDS (gathered through pi, §3.2) and shared by both
-// tiles, the two column parts add their accumulators in LDS. All packed-weight loads of a wave are
+// Workgroup: 16 wavefronts = T weight tiles of 64 rows (4 waves of 16 rows each) x 4/T column
+// parts. It owns a range of column groups (split-K over workgroups) and one chunk of activation
+// rows; the column parts add their accumulators in LDS. Up to 16 rows the activations of its
+// columns are staged once in LDS (gathered through pi below 8 rows, §3.2) and shared by the tiles;
+// from 17 rows they stream through LDS one column group per part at a time (1 x 4), so a 64-row
+// tile can take every group of its row without split-K. All packed-weight loads of a wave are
 // issued up front through range-checked buffer loads, as in the batch-one kernel.
 #include <algorithm>
 #include <mutex>
@@ -285,23 +287,23 @@ __device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint
   // ... straight into LDS. Lane l of a piece fills row r0 + l / 16, slot l % 16, i.e. chunk
   // (l % 16) ^ (row % 16) of the row. Groups past a part's range read zeros.
   constexpr int kSlabRows = NT * 16;
-  const int gpp_s = (ngl + 3) / 4;
+  const int giters = (ngl + 3) / 4;
   auto stage = [&](int it) {
     if constexpr (kStream) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const int piece = wave + 16 * t;
-        const int pp_ = piece / (kSlabRows / 4);
+        const int spart = piece / (kSlabRows / 4);
         const int r0 = (piece % (kSlabRows / 4)) * 4;
         const int row = r0 + (lane >> 4);
         const int chunk = (lane & 15) ^ (row & 15);
-        const int gi = pp_ * gpp_s + it;
-        const bool ok = it < gpp_s && gi < ngl;
+        const int gi = spart * giters + it;
+        const bool ok = it < giters && gi < ngl;
         const uint32_t off =
             ok ? (uint32_t)(((int64_t)row * A.ldx + c0 + gi * kGroupCols + chunk * 8) * 2)
                : kNowhere;
         uint8_t* dst = reinterpret_cast<uint8_t*>(xs) +
-                       ((uint32_t)(((it & 1) * 4 + pp_) * kSlabRows + r0) * 256u);
+                       ((uint32_t)(((it & 1) * 4 + spart) * kSlabRows + r0) * 256u);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rs, (__attribute__((address_space(3))) void*)dst,
                                                  16, off, 0, 0, 0);
       }
@@ -396,7 +398,7 @@ __device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint
     // others at the barrier, after which the other buffer is free for iteration it + 1.
 #pragma unroll
     for (int it = 0; it < kGMaxUnits; ++it) {
-      if (it < gpp_s) {
+      if (it < giters) {
         if (it == 0)
           asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NT + 2 * kGMaxUnits)
                        : "memory");
@@ -405,7 +407,7 @@ __device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint
                        : "memory");
         else
           asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (it >= 1 && it + 1 < gpp_s) stage(it + 1);
+        if (it >= 1 && it + 1 < giters) stage(it + 1);
         if (it < ngp) {
           const uint8_t* abase = reinterpret_cast<const uint8_t*>(xs) +
                                  (uint32_t)(((it & 1) * 4 + part) * kSlabRows) * 256u;
@@ -1082,11 +1084,11 @@ size_t lds_for(int L, int nt, int gs, int T) {
 
 // Workgroup shape and groups per split (a workgroup fills a compute unit, so a launch should fit
 // in one workgroup per compute unit):
-//   1. 8 to 16 activation rows (read as whole vectors, not gathered): 1 x 4 with every column
-//      group in one split when that fits (no split-K at all; more rows would not fit the LDS with
-//      twenty groups, and with fewer the per-thread gather of twenty groups costs more than the
-//      split-K pass it saves);
-//   2. else 2 x 2 with the fewest groups per split that fit, within the LDS budget.
+//   1. 17 rows or more: 1 x 4 with streamed activations (below);
+//   2. 8 to 16 activation rows (read as whole vectors, not gathered): 1 x 4 with every column
+//      group in one split when that fits (no split-K at all; with fewer rows the per-thread
+//      gather of twenty groups costs more than the split-K pass it saves);
+//   3. else 2 x 2 with the fewest groups per split that fit, within the LDS budget.
 void plan(GemmArgs& A, int M) {
   A.rt = ceil_div(A.d_out, kTileRows);
   A.ng = A.d_in / kGroupCols;
