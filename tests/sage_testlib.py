@@ -55,7 +55,7 @@ def ulp_distance(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
 
 
 # ------------------------------------------------------------------------------------------------
-# Output bounds. The contract bound is the one the task states; the tight bound is what the
+# Output bounds. The contract bound is the fixed 2e-3 relative bound; the tight bound is what the
 # arithmetic allows, so that one wrong subvector (a wrong codeword index, sign or radius code)
 # exceeds it.
 # ------------------------------------------------------------------------------------------------

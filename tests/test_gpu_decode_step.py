@@ -6,7 +6,7 @@ previous stage's fp16 outputs as the kernels produced them:
   producers (RMSNorm, silu*mul, written in the next matrix's stored order)
                  within 1 fp16 ulp of the correctly rounded float64 value;
   products       the tight per-element bound of the batch-one kernel (sage_testlib) against the
-                 oracle product of the same input, and the task's contract bound.
+                 oracle product of the same input, and the 2e-3 relative contract bound.
 The attention between the two chains is PyTorch's; the o projection that follows it gathers its
 input through pi and is checked the same way. Whole steps are checked for finiteness and
 bit-for-bit repetition. Weights and inputs are the seeded synthetic decoder layer (workloads/).

@@ -5,7 +5,7 @@ Bars (stated in the method's terms, SAGE paper §3.1 Eq. (1)-(2)):
                      (oracle/packing.py, written from the format description).
   dequant            within 1 fp16 ulp of the correctly rounded decode (+0 == -0); the fp64 device
                      decode is expected to be exact.
-  products           the task's contract bound, max |y - y_ref| <= 2e-3 * max_r sum_c |W_hat||x|
+  products           the contract bound, max |y - y_ref| <= 2e-3 * max_r sum_c |W_hat||x|
                      per output vector, AND a tight per-element bound derived from the arithmetic
                      (see sage_testlib: one fp16 rounding of the output, the fp32 accumulation and,
                      for the batch-one kernel, its radius arithmetic) that one wrong subvector
