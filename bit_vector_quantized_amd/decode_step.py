@@ -140,14 +140,28 @@ class DecodeStack:
         inv_freq = 1.0 / (dims.rope_theta ** (
             torch.arange(0, half, dtype=torch.float64, device="cuda") / half))
         ang = torch.arange(n, dtype=torch.float64, device="cuda")[:, None] * inv_freq[None, :]
-        self.cos = torch.cos(ang).float()
-        self.sin = torch.sin(ang).float()
+        # rotation of a head as x * cos2 + roll(x, half) * sin2: cos2 = [cos, cos], sin2 = [-sin, sin]
+        cos, sin = torch.cos(ang).float(), torch.sin(ang).float()
+        self.cos2 = torch.cat((cos, cos), dim=1).contiguous()
+        self.sin2 = torch.cat((-sin, sin), dim=1).contiguous()
+        # per-head norm weights of the 32 query and 8 key heads as one [40, head_dim] block, the
+        # query rows scaled by head_dim^-1/2 (the attention scale, folded in once)
+        scale = dims.head_dim ** -0.5
+        self.qk_w = [torch.cat((lw.q_norm.float().expand(dims.heads, dims.head_dim) * scale,
+                                lw.k_norm.float().expand(dims.kv_heads, dims.head_dim)))
+                     .contiguous() for lw in layers]
 
     # -- the linear chains (libsage kernels) --------------------------------------------------
     def attn_in(self, lw: LayerWeights, h):
-        """a = RMSNorm(h) in q/k/v's stored order; q, k, v (fp16) from one launch."""
-        a = sage.rmsnorm_permute(h, lw.ln_attn, self.dims.eps, lw.pi_attn)
-        q, k, v = sage.gemv_multi([lw.q, lw.k, lw.v], [a, a, a])
+        """a = RMSNorm(h) in q/k/v's stored order; q, k, v (fp16) from one launch, written next to
+        each other in one buffer (so the query and key heads form one block)."""
+        import torch
+        d = self.dims
+        a = sage.rmsnorm_permute(h, lw.ln_attn, d.eps, lw.pi_attn)
+        nq, nk = d.heads * d.head_dim, d.kv_heads * d.head_dim
+        qkv = torch.empty(nq + 2 * nk, dtype=torch.float16, device=h.device)
+        q, k, v = qkv[:nq], qkv[nq:nq + nk], qkv[nq + nk:]
+        sage.gemv_multi([lw.q, lw.k, lw.v], [a, a, a], ys=[q, k, v])
         return a, q, k, v
 
     def mlp(self, lw: LayerWeights, h):
@@ -160,35 +174,31 @@ class DecodeStack:
         return b, g, u, m, d
 
     # -- attention (PyTorch) --------------------------------------------------------------------
-    def _head_norm(self, t, w):
-        import torch.nn.functional as F
-        return F.rms_norm(t.float(), (self.dims.head_dim,), w.float(), self.dims.eps)
-
-    def _rope(self, t, pos: int):
-        import torch
-        cos, sin = self.cos[pos], self.sin[pos]
-        t1, t2 = t[..., : t.shape[-1] // 2], t[..., t.shape[-1] // 2:]
-        return torch.cat((t1 * cos - t2 * sin, t2 * cos + t1 * sin), dim=-1)
-
     def attention(self, li: int, lw: LayerWeights, q, k, v):
         """Attention output (fp16 [heads * head_dim], original order) for the token at self.pos."""
         import torch
         import torch.nn.functional as F
         d = self.dims
-        qh = self._rope(self._head_norm(q.view(d.heads, d.head_dim), lw.q_norm), self.pos).half()
-        kh = self._rope(self._head_norm(k.view(d.kv_heads, d.head_dim), lw.k_norm), self.pos)
-        self.kcache[li, :, self.pos] = kh.half()
-        self.vcache[li, :, self.pos] = v.view(d.kv_heads, d.head_dim)
+        D, nh, g = d.head_dim, d.heads + d.kv_heads, d.heads // d.kv_heads
+        if k.data_ptr() == q.data_ptr() + q.numel() * q.element_size():
+            qk = torch.as_strided(q, (nh, D), (D, 1))      # q and k adjacent (attn_in)
+        else:
+            qk = torch.cat((q, k)).view(nh, D)
+        # per-head RMSNorm (query rows carry the attention scale) and the rotation, all 40 heads
+        x = F.rms_norm(qk.float(), (D,), None, d.eps) * self.qk_w[li]
+        x = torch.addcmul(x * self.cos2[self.pos], torch.roll(x, D // 2, dims=1), self.sin2[self.pos])
+        self.kcache[li, :, self.pos] = x[d.heads:]        # rounded to fp16 by the copy
+        self.vcache[li, :, self.pos] = v.view(d.kv_heads, D)
         n = self.pos + 1
-        # grouped-query attention for one query as two batched fp16 products: the 4 query heads of
-        # a key/value head form the columns of one operand (a contiguous [kv_heads, head_dim, 4]),
-        # the cached keys and values are read in place
-        g = d.heads // d.kv_heads
-        qg = qh.view(d.kv_heads, g, d.head_dim).transpose(1, 2).contiguous()
-        s = torch.matmul(self.kcache[li, :, :n], qg).float() * (d.head_dim ** -0.5)
-        pr = torch.softmax(s, dim=1).half()                         # [kv_heads, n, g]
-        o = torch.matmul(pr.transpose(1, 2).contiguous(), self.vcache[li, :, :n])
-        return o.reshape(d.heads * d.head_dim)
+        # grouped-query attention for one query as two batched fp16 products: the g query heads of
+        # a key/value head form the columns of one operand [kv_heads, head_dim, g]; the cached keys
+        # and values are read in place
+        qg = torch.empty((d.kv_heads, D, g), dtype=torch.float16, device=q.device)
+        qg.copy_(x[:d.heads].view(d.kv_heads, g, D).transpose(1, 2))
+        s = torch.matmul(self.kcache[li, :, :n], qg)                 # [kv_heads, n, g]
+        pr = torch.softmax(s, dim=1, dtype=torch.float32).half()
+        o = torch.matmul(pr.transpose(1, 2), self.vcache[li, :, :n])  # [kv_heads, g, head_dim]
+        return o.reshape(d.heads * D)
 
     def layer(self, li: int, h):
         lw = self.layers[li]
