@@ -158,7 +158,9 @@ int sage_gemv_multi(const sage_matrix_t* mats, const uint16_t* const* xs, uint16
  *       When the matrix has pi = NULL (X already in stored column order, e.g. written permuted
  *       by its producer) and X is 16-byte aligned with ldx a multiple of 8, X is read in place
  *       and no reorder runs. The workspace must be zero-filled before its first use; every call
- *       leaves it ready for the next. Calls that share a workspace must not overlap.
+ *       leaves it ready for the next call with the same d_out, d_in and M (where the arrival
+ *       counters sit depends on them: zero it again before using it for another shape or M).
+ *       Calls that share a workspace must not overlap.
  */
 int sage_gemm_small_workspace_bytes(const sage_matrix_t* m, int M, size_t* bytes);
 int sage_gemm_small(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, uint16_t* Y,
