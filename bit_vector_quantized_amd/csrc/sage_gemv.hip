@@ -238,16 +238,18 @@ __device__ __forceinline__ float decode_unit(const Unit& U, uint32_t xa, int l16
   return acc;
 }
 
-// The whole workgroup: chunks [c0, c0 + nc) of one product. kGather: pi may be non-NULL.
+// The whole workgroup: chunks [c0, c0 + nc) of one product. kGather: pi may be non-NULL. kEarly:
+// the launch has at most one workgroup per compute unit (see the order of work below).
 //
 // Order of work. The codebook (in registers of waves 0-3) and the input (in LDS) are waited for
-// first, and the table is written, before any packed unit is requested: a compute unit returns
-// load data in request order across its waves, so small loads queued behind the packed stream
-// would arrive only with it, and a wave whose requests wait for the memory pipeline to accept them
-// would hold every other wave at a later barrier. Each wave then requests its units and decodes
-// them as they land. Every VALU instruction outside the decode loop runs on all 16 wavefronts, so
+// first: a compute unit returns load data in request order across its waves, so small loads
+// queued behind a packed stream would arrive only with it. With two workgroups per compute unit
+// the table is also written before any packed unit is requested, so the first workgroup's stream
+// does not overtake the second's small loads. With one (kEarly), each wave requests the units it
+// steps through as soon as the small loads have landed, and the table build (and the gather)
+// overlap their latency. Each wave then decodes its units as they land. Every VALU instruction outside the decode loop runs on all 16 wavefronts, so
 // the per-thread set-up is kept short and done while the first loads are in flight.
-template <int L, bool kGather>
+template <int L, bool kGather, bool kEarly>
 __device__ __attribute__((always_inline)) void gemv_wg(const uint8_t* packed, const uint16_t* codebook, const int32_t* pi,
                         const uint16_t* x, uint16_t* y, int d_out, int d_in, int c0, int nc) {
   using S = Split<L>;
@@ -326,6 +328,31 @@ __device__ __attribute__((always_inline)) void gemv_wg(const uint8_t* packed, co
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
+  // Packed units: kRing per lane group in flight; unit k + kRing is requested once unit k is
+  // decoded. A range shorter than its wave's longest steps one unit past its end. That unit is
+  // read as zeros and decoded with every lane active (its zero grid adds exactly 0): the DPP row
+  // broadcasts of the dot steps gave wrong sums when run under a partial exec mask, even with every
+  // lane of the row active. Its inputs are those of the group after the range's last one in the
+  // same chunk, or of group 0 when the range ends at its chunk's end (a range covers at most a
+  // chunk's units, so never the end of a second chunk): always staged, finite inputs.
+  auto request = [&](Unit& u, int k) {
+    const uint32_t step = (uint32_t)k * (uint32_t)kBlockBytes;
+    const bool second = k >= W.kb;
+    const bool ok = k < W.cnt;
+    const uint32_t po = ok ? (second ? pa1 : pa0) + step : kNowhere;
+    const uint32_t so = ok ? (second ? sa1 : sa0) + step : kNowhere;
+    u.a = __builtin_amdgcn_raw_buffer_load_b128(wv, po, 0, kNonTemporal);
+    u.b = __builtin_amdgcn_raw_buffer_load_b128(wv, po + (uint32_t)kPlaneB, 0, kNonTemporal);
+    u.s = __builtin_amdgcn_raw_buffer_load_b64(wv, so, 0, kNonTemporal);
+  };
+  Unit ring[kRing];
+  if constexpr (kEarly) {
+    // only units the wave steps through (the others are never decoded)
+#pragma unroll
+    for (int k = 0; k < kRing; ++k)
+      if (k < cntw) request(ring[k], k);
+  }
+
   // 3. LDS set-up: waves 0-3 write the sign-applied codeword table (wave w the (half, signs)
   // combinations w, w + 4, ..., for every codeword it holds); gathering, every thread puts input
   // pieces into stored order.
@@ -375,26 +402,12 @@ __device__ __attribute__((always_inline)) void gemv_wg(const uint8_t* packed, co
   }
   __syncthreads();
 
-  // 4. The packed units: kRing per lane group in flight; unit k + kRing is requested once unit k
-  // is decoded. A range shorter than its wave's longest steps one unit past its end. That unit is
-  // read as zeros and decoded with every lane active (its zero grid adds exactly 0): the DPP row
-  // broadcasts of the dot steps gave wrong sums when run under a partial exec mask, even with every
-  // lane of the row active. Its inputs are those of the group after the range's last one in the
-  // same chunk, or of group 0 when the range ends at its chunk's end (a range covers at most a
-  // chunk's units, so never the end of a second chunk): always staged, finite inputs.
-  auto request = [&](Unit& u, int k) {
-    const uint32_t step = (uint32_t)k * (uint32_t)kBlockBytes;
-    const bool second = k >= W.kb;
-    const bool ok = k < W.cnt;
-    const uint32_t po = ok ? (second ? pa1 : pa0) + step : kNowhere;
-    const uint32_t so = ok ? (second ? sa1 : sa0) + step : kNowhere;
-    u.a = __builtin_amdgcn_raw_buffer_load_b128(wv, po, 0, kNonTemporal);
-    u.b = __builtin_amdgcn_raw_buffer_load_b128(wv, po + (uint32_t)kPlaneB, 0, kNonTemporal);
-    u.s = __builtin_amdgcn_raw_buffer_load_b64(wv, so, 0, kNonTemporal);
-  };
-  Unit ring[kRing];
+  // 4. The packed units (requested here with two workgroups per compute unit), decoded as they
+  // land.
+  if constexpr (!kEarly) {
 #pragma unroll
-  for (int k = 0; k < kRing; ++k) request(ring[k], k);
+    for (int k = 0; k < kRing; ++k) request(ring[k], k);
+  }
   // only a range that really crosses into a second chunk switches sums
   const bool split = W.kb < W.cnt;
   float acc = 0.0f, acc0 = 0.0f;
@@ -453,15 +466,15 @@ __device__ __forceinline__ void by_split(int L, F&& f) {
   }
 }
 
-template <bool kGather>
+template <bool kGather, bool kEarly>
 __global__ void __launch_bounds__(kThreads) gemv_kernel(GemvArgs A) {
   const uint32_t e = A.wg[blockIdx.x];
   const Prod& P = A.prod[e & 15u];
   const int nc = (int)((e >> 4) & 63u) + 1;
   const int c0 = (int)(e >> 10);
   by_split(P.L, [&](auto Lc) {
-    gemv_wg<decltype(Lc)::value, kGather>(P.packed, P.codebook, P.pi, P.x, P.y, P.d_out, P.d_in,
-                                          c0, nc);
+    gemv_wg<decltype(Lc)::value, kGather, kEarly>(P.packed, P.codebook, P.pi, P.x, P.y, P.d_out,
+                                                  P.d_in, c0, nc);
   });
 }
 
@@ -471,7 +484,7 @@ __device__ __attribute__((noinline)) void moe_pass(const uint8_t* packed, const 
                                                   uint16_t* y, int d_out, int d_in, int L, int c0,
                                                   int nc) {
   by_split(L, [&](auto Lc) {
-    gemv_wg<decltype(Lc)::value, true>(packed, codebook, pi, x, y, d_out, d_in, c0, nc);
+    gemv_wg<decltype(Lc)::value, true, true>(packed, codebook, pi, x, y, d_out, d_in, c0, nc);
   });
 }
 
@@ -509,7 +522,7 @@ __global__ void __launch_bounds__(kThreads) moe_kernel(MoeArgs A) {
   if (cend - cbeg <= kMaxChunks) {
     if (cend > cbeg) {
       by_split(L, [&](auto Lc) {
-        gemv_wg<decltype(Lc)::value, true>(packed, codebook, pi, x, y, d_out, d_in, cbeg,
+        gemv_wg<decltype(Lc)::value, true, true>(packed, codebook, pi, x, y, d_out, d_in, cbeg,
                                            cend - cbeg);
       });
     }
@@ -544,6 +557,7 @@ struct Plan {
   int nwg = 0;
   size_t lds = 0;
   bool gather = false;
+  bool early = false;   // at most one workgroup per compute unit: request at the first barrier
 };
 
 int plan(const sage_matrix_t* mats, const uint16_t* const* xs, uint16_t* const* ys, int n,
@@ -587,6 +601,7 @@ int plan(const sage_matrix_t* mats, const uint16_t* const* xs, uint16_t* const* 
   }
   if (nwg > kMaxWgs) return SAGE_ERR_SHAPE;
   P->nwg = (int)nwg;
+  P->early = nwg <= cus;
   P->lds = 0;
   P->gather = false;
   int w = 0;
@@ -616,12 +631,10 @@ int plan(const sage_matrix_t* mats, const uint16_t* const* xs, uint16_t* const* 
 }
 
 int launch(const Plan& P, sage_stream_t stream) {
-  if (P.gather)
-    hipLaunchKernelGGL(gemv_kernel<true>, dim3(P.nwg), dim3(kThreads), P.lds, (hipStream_t)stream,
-                       P.args);
-  else
-    hipLaunchKernelGGL(gemv_kernel<false>, dim3(P.nwg), dim3(kThreads), P.lds, (hipStream_t)stream,
-                       P.args);
+  typedef void (*GemvFn)(GemvArgs);
+  const GemvFn fn = P.gather ? (P.early ? gemv_kernel<true, true> : gemv_kernel<true, false>)
+                             : (P.early ? gemv_kernel<false, true> : gemv_kernel<false, false>);
+  hipLaunchKernelGGL(fn, dim3(P.nwg), dim3(kThreads), P.lds, (hipStream_t)stream, P.args);
   return hip_status();
 }
 
@@ -633,10 +646,12 @@ void lds_limit_set() {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   std::lock_guard<std::mutex> lock(mu);
   if (!done[dev]) {
-    (void)hipFuncSetAttribute((const void*)gemv_kernel<false>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    (void)hipFuncSetAttribute((const void*)gemv_kernel<true>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    const void* fns[4] = {(const void*)gemv_kernel<false, false>,
+                          (const void*)gemv_kernel<false, true>,
+                          (const void*)gemv_kernel<true, false>,
+                          (const void*)gemv_kernel<true, true>};
+    for (const void* f : fns)
+      (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     (void)hipFuncSetAttribute((const void*)moe_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                               160 * 1024);
     done[dev] = true;
