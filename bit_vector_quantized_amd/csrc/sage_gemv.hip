@@ -2,7 +2,7 @@
 // y = W_hat x with W_hat decoded on the fly from its 18-bit subvector codes (§3.1 Eq. (1)-(3)).
 //
 // Work decomposition. Rows are taken in chunks of 16 (a quarter of a packed row tile). A workgroup
-// of 1024 threads (16 wavefronts, one workgroup per compute unit) owns whole rows: a run of chunks
+// of 1024 threads (16 wavefronts; one or two per compute unit) owns whole rows: a run of chunks
 // of one product, so no partial sum ever leaves the compute unit (no split-K hand-off between
 // workgroups). Its (chunk, 128-column group) units, chunk-major, are cut into 64 contiguous ranges
 // whose lengths differ by at most one, one per lane group of 16 lanes; lane l of a group owns row l
@@ -574,13 +574,21 @@ int plan(const sage_matrix_t* mats, const uint16_t* const* xs, uint16_t* const* 
     total_units += units[i];
     total_chunks += chunks[i];
   }
-  // workgroups: two per compute unit when two fit in its LDS (eight wavefronts per SIMD hide the
-  // latency of the table reads better than four), else one; no more than there are chunks, and at
-  // least enough that no workgroup has more than kMaxChunks chunks
+  // workgroups: two per compute unit when two fit in its LDS, every compute unit gets two (at
+  // least twice as many chunks as units) and no product gathers its input: eight wavefronts per
+  // SIMD then hide the latency of the table reads better than four. Otherwise one, which requests
+  // its packed units as soon as its small loads have landed (measured: q|k|v's 384 chunks 5.14 ->
+  // 4.90 us with one; gate|up's 1216 chunks 7.38 us with two, 7.76 us with one, and with pi
+  // gathered 8.17 us with two, 8.02 us with one). No more workgroups than there are chunks, and at
+  // least enough that no workgroup has more than kMaxChunks chunks.
   uint32_t lds_max = 0;
-  for (int i = 0; i < n; ++i)
+  bool any_gather = false;
+  for (int i = 0; i < n; ++i) {
     lds_max = std::max(lds_max, lds_total(mats[i].log2K, mats[i].d_in, mats[i].pi != nullptr));
-  const int per_cu = lds_max <= kMaxLds / 2 ? 2 : 1;
+    any_gather = any_gather || mats[i].pi != nullptr;
+  }
+  const int per_cu =
+      lds_max <= kMaxLds / 2 && !any_gather && total_chunks >= 2 * (int64_t)cus ? 2 : 1;
   int64_t G = std::min<int64_t>((int64_t)cus * per_cu, total_chunks);
   std::vector<int64_t> g(n);
   std::vector<std::pair<double, int>> rema;
