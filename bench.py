@@ -307,6 +307,46 @@ def stream_reference(nbytes):
             "one_gib_launch_gbs": round((1 << 30) / (gib_us * 1e-6) / 1e9, 1)}
 
 
+def launch_floors(bench):
+    """Per-launch floors measured the same way as the layer's launches (a graph of back-to-back
+    launches timed with HIP events): an empty launch (sage_stream_read of 16 bytes: dispatch and
+    completion only), and for each launch of the step a streaming read of its packed bytes."""
+    import torch
+    import bit_vector_quantized_amd as sage
+    pool = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def graph_us(nbytes):
+        n = (nbytes + 15) // 16 * 16
+        windows = min(64, (1 << 30) // n)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for w in range(windows):
+                    sage.stream_read(pool[w * n:(w + 1) * n], sink=sink)
+        torch.cuda.synchronize()
+        reps = 10
+        with torch.cuda.stream(s):
+            g.replay()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(s)
+            for _ in range(reps):
+                g.replay()
+            b.record(s)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / (reps * windows)
+
+    out = {"empty_launch_us": round(graph_us(16), 3), "stream_read_us": {}}
+    for key, names, _ in LayerBench.LAUNCHES:
+        nb = sum(packed_weight_bytes(bench.base[n]) for n in names)
+        out["stream_read_us"][key] = round(graph_us(nb), 3)
+    del pool
+    return out
+
+
 # ------------------------------------------------------------------------------------------------
 # CPU oracle baseline
 # ------------------------------------------------------------------------------------------------
@@ -692,6 +732,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    log("[bench] timing the per-launch floors")
+    line["config"]["floors"] = launch_floors(bench)
     log("[bench] timing the streaming-read reference")
     ref = stream_reference(bench.dom_bytes)
     if roofline is not None:
