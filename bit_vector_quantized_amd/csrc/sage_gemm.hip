@@ -596,7 +596,9 @@ __device__ void gemm_body(const GemmArgs& A, int rp, int split, int mchunk, uint
   if (tid == 0) counter_reset(counter);
 }
 
-template <int NT, bool kVec, int kGT, bool kStream = false>
+// One kernel per split (log2 K = L compiled in): a wave runs through a third of the code a switch
+// over the split would give it (fewer instruction-cache misses while the workgroups start).
+template <int NT, bool kVec, int kGT, bool kStream, int L>
 __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs A) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int per_chunk = A.rpairs * A.S;
@@ -604,16 +606,21 @@ __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs A) {
   const int local = blockIdx.x - mchunk * per_chunk;
   const int rp = local / A.S;
   const int split = local - rp * A.S;
-  switch (A.L) {
-    case 4: gemm_body<4, NT, kVec, kGT, kStream>(A, rp, split, mchunk, smem); break;
-    case 5: gemm_body<5, NT, kVec, kGT, kStream>(A, rp, split, mchunk, smem); break;
-    case 6: gemm_body<6, NT, kVec, kGT, kStream>(A, rp, split, mchunk, smem); break;
-    case 7: gemm_body<7, NT, kVec, kGT, kStream>(A, rp, split, mchunk, smem); break;
-    default: gemm_body<8, NT, kVec, kGT, kStream>(A, rp, split, mchunk, smem); break;
-  }
+  gemm_body<L, NT, kVec, kGT, kStream>(A, rp, split, mchunk, smem);
 }
 
 typedef void (*GemmFn)(GemmArgs);
+
+template <int NT, bool kVec, int kGT, bool kStream = false>
+GemmFn gemm_fn(int L) {
+  switch (L) {
+    case 4: return gemm_kernel<NT, kVec, kGT, kStream, 4>;
+    case 5: return gemm_kernel<NT, kVec, kGT, kStream, 5>;
+    case 6: return gemm_kernel<NT, kVec, kGT, kStream, 6>;
+    case 7: return gemm_kernel<NT, kVec, kGT, kStream, 7>;
+    default: return gemm_kernel<NT, kVec, kGT, kStream, 8>;
+  }
+}
 
 // ------------------------------------------------------------------------------------------------
 // Prefill-sized batches (SAGE paper §3.5 / Fig. 6b: decode each weight once per output tile and
@@ -1318,26 +1325,26 @@ int gemm_small_run(const sage_matrix_t* m, const uint16_t* X, int M, int ldx, ui
   const int nt = tiles_for(M);
   const size_t lds = A.stream ? stream_lds(A.L, nt) : lds_for(A.L, nt, A.gs, A.tiles);
   const unsigned grid = (unsigned)(A.mchunks * A.rpairs * A.S);
-  // Each instantiation gets its LDS limit raised once (slot = shape * 4 + variant).
-  static bool attr_set[8] = {};
+  // Each instantiation gets its LDS limit raised once (slot = variant, split).
+  static bool attr_set[8][9] = {};
   auto launch = [&](GemmFn kern, int slot) {
-    if (!attr_set[slot]) {
+    if (!attr_set[slot][A.L]) {
       (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-      attr_set[slot] = true;
+      attr_set[slot][A.L] = true;
     }
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kGThreads), lds, hs, A);
   };
   if (A.stream) {  // nt == 2 or 4, 1 x 4 with streamed activations
-    if (nt == 2) launch(gemm_kernel<2, true, 1, true>, 2);
-    else launch(gemm_kernel<4, true, 1, true>, 3);
+    if (nt == 2) launch(gemm_fn<2, true, 1, true>(A.L), 2);
+    else launch(gemm_fn<4, true, 1, true>(A.L), 3);
   } else if (A.tiles == 1) {  // nt == 1, whole-vector rows
-    launch(gemm_kernel<1, true, 1>, 1);
+    launch(gemm_fn<1, true, 1>(A.L), 1);
   } else {
-    if (!A.vec_x) launch(gemm_kernel<1, false, 2>, 4);  // fewer than kPermuteMinRows rows: nt == 1
-    else if (nt == 1) launch(gemm_kernel<1, true, 2>, 5);
-    else if (nt == 2) launch(gemm_kernel<2, true, 2>, 6);
-    else launch(gemm_kernel<4, true, 2>, 7);
+    if (!A.vec_x) launch(gemm_fn<1, false, 2>(A.L), 4);  // fewer than kPermuteMinRows rows: nt == 1
+    else if (nt == 1) launch(gemm_fn<1, true, 2>(A.L), 5);
+    else if (nt == 2) launch(gemm_fn<2, true, 2>(A.L), 6);
+    else launch(gemm_fn<4, true, 2>(A.L), 7);
   }
   return hip_status();
 }

@@ -466,16 +466,24 @@ __device__ __forceinline__ void by_split(int L, F&& f) {
   }
 }
 
-template <bool kGather, bool kEarly>
+// kL: the split (log2 K) of every product of the launch, compiled in; 0 when the products' splits
+// differ and each workgroup selects its product's at run time. One split per kernel keeps the code a
+// wave runs through about a third as long (fewer instruction-cache misses while the workgroups
+// start; measured: every layer launch 0.05-0.14 us shorter).
+template <bool kGather, bool kEarly, int kL>
 __global__ void __launch_bounds__(kThreads) gemv_kernel(GemvArgs A) {
   const uint32_t e = A.wg[blockIdx.x];
   const Prod& P = A.prod[e & 15u];
   const int nc = (int)((e >> 4) & 63u) + 1;
   const int c0 = (int)(e >> 10);
-  by_split(P.L, [&](auto Lc) {
-    gemv_wg<decltype(Lc)::value, kGather, kEarly>(P.packed, P.codebook, P.pi, P.x, P.y, P.d_out,
-                                                  P.d_in, c0, nc);
-  });
+  if constexpr (kL != 0) {
+    gemv_wg<kL, kGather, kEarly>(P.packed, P.codebook, P.pi, P.x, P.y, P.d_out, P.d_in, c0, nc);
+  } else {
+    by_split(P.L, [&](auto Lc) {
+      gemv_wg<decltype(Lc)::value, kGather, kEarly>(P.packed, P.codebook, P.pi, P.x, P.y, P.d_out,
+                                                    P.d_in, c0, nc);
+    });
+  }
 }
 
 // One pass of a routed-expert workgroup (a function of its own, so the kernel holds one copy).
@@ -558,6 +566,7 @@ struct Plan {
   size_t lds = 0;
   bool gather = false;
   bool early = false;   // at most one workgroup per compute unit: request at the first barrier
+  int L = 0;            // the products' common split, or 0 when they differ
 };
 
 int plan(const sage_matrix_t* mats, const uint16_t* const* xs, uint16_t* const* ys, int n,
@@ -612,6 +621,9 @@ int plan(const sage_matrix_t* mats, const uint16_t* const* xs, uint16_t* const* 
   P->early = nwg <= cus;
   P->lds = 0;
   P->gather = false;
+  P->L = mats[0].log2K;
+  for (int i = 1; i < n; ++i)
+    if (mats[i].log2K != P->L) P->L = 0;
   int w = 0;
   for (int i = 0; i < n; ++i) {
     const sage_matrix_t& m = mats[i];
@@ -638,10 +650,19 @@ int plan(const sage_matrix_t* mats, const uint16_t* const* xs, uint16_t* const* 
   return SAGE_OK;
 }
 
+typedef void (*GemvFn)(GemvArgs);
+
+// The kernels of one (gather, early) pair: index 0 selects the split at run time, 1 + L - 4 has
+// split L compiled in.
+template <bool kGather, bool kEarly>
+constexpr GemvFn kGemvBySplit[6] = {gemv_kernel<kGather, kEarly, 0>, gemv_kernel<kGather, kEarly, 4>,
+                                    gemv_kernel<kGather, kEarly, 5>, gemv_kernel<kGather, kEarly, 6>,
+                                    gemv_kernel<kGather, kEarly, 7>, gemv_kernel<kGather, kEarly, 8>};
+constexpr const GemvFn* kGemvFns[4] = {kGemvBySplit<false, false>, kGemvBySplit<false, true>,
+                                       kGemvBySplit<true, false>, kGemvBySplit<true, true>};
+
 int launch(const Plan& P, sage_stream_t stream) {
-  typedef void (*GemvFn)(GemvArgs);
-  const GemvFn fn = P.gather ? (P.early ? gemv_kernel<true, true> : gemv_kernel<true, false>)
-                             : (P.early ? gemv_kernel<false, true> : gemv_kernel<false, false>);
+  const GemvFn fn = kGemvFns[(P.gather ? 2 : 0) + (P.early ? 1 : 0)][P.L ? P.L - 3 : 0];
   hipLaunchKernelGGL(fn, dim3(P.nwg), dim3(kThreads), P.lds, (hipStream_t)stream, P.args);
   return hip_status();
 }
@@ -654,12 +675,10 @@ void lds_limit_set() {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   std::lock_guard<std::mutex> lock(mu);
   if (!done[dev]) {
-    const void* fns[4] = {(const void*)gemv_kernel<false, false>,
-                          (const void*)gemv_kernel<false, true>,
-                          (const void*)gemv_kernel<true, false>,
-                          (const void*)gemv_kernel<true, true>};
-    for (const void* f : fns)
-      (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    for (const GemvFn* fns : kGemvFns)
+      for (int k = 0; k < 6; ++k)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(fns[k]),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     (void)hipFuncSetAttribute((const void*)moe_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                               160 * 1024);
     done[dev] = true;
