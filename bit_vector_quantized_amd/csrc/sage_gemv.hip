@@ -7,8 +7,8 @@
 // workgroups). Its (chunk, 128-column group) units, chunk-major, are cut into 64 contiguous ranges
 // whose lengths differ by at most one, one per lane group of 16 lanes; lane l of a group owns row l
 // of the chunk it is working on. A range crosses at most one chunk boundary, so a lane keeps two sums.
-// At the end one thread per row adds the sums of the ranges covering its chunk in range order (a
-// fixed order: results are reproducible bit for bit) and one rounding to fp16 gives y.
+// At the end the sums of the ranges covering a row's chunk are added in a fixed order (results are
+// reproducible bit for bit) and one rounding to fp16 gives y.
 //
 // Decode. The workgroup builds, once, a table of sign-applied codeword halves in LDS:
 // T[h][s][z] (h = first or second half of the 8-wide codeword, s = 4 sign bits, z = codeword) holds
@@ -427,9 +427,10 @@ __device__ __attribute__((always_inline)) void gemv_wg(const uint8_t* packed, co
     }
   }
 
-  // 5. Range sums to LDS (slot 0: the range's first chunk, slot 1: its second), then one thread
-  // per row adds the sums of the ranges that cover its chunk (a contiguous run lo..hi) in range
-  // order: a fixed order, so results are reproducible bit for bit.
+  // 5. Range sums to LDS (slot 0: the range's first chunk, slot 1: its second). A row's sum is
+  // over the ranges that cover its chunk, a contiguous run lo..hi (at most 64, and at most the
+  // chunk's ng units). Both ways below add them in a fixed order, so results are reproducible bit
+  // for bit.
   {
     const uint32_t a = PB + (uint32_t)(rw * kChunkRows + l16) * 4u;
     *(__attribute__((address_space(3))) float*)(size_t)a = split ? acc0 : acc;
@@ -437,21 +438,70 @@ __device__ __attribute__((always_inline)) void gemv_wg(const uint8_t* packed, co
         split ? acc : 0.0f;
   }
   __syncthreads();
-  if (tid < nc * kChunkRows) {
-    const int cl = tid >> 4, rr = tid & 15;
-    const int base = nu >> 6, rem = nu & 63;
-    const int ub = cl * ng;   // the chunk's first unit
-    const int lo = range_of(ub, base, rem);
-    const int hi = range_of(ub + ng - 1, base, rem);
-    // lo may have started in the previous chunk: its sum for this chunk is its second one
-    const uint32_t seg = lo * base + min(lo, rem) < ub ? 1u : 0u;
-    typedef __attribute__((address_space(3))) const float lds_f;
-    float sum = *(lds_f*)(size_t)(PB + ((seg * kLaneGroups + (uint32_t)lo) * kChunkRows + rr) * 4u);
+  typedef __attribute__((address_space(3))) const float lds_f;
+  const int base = nu >> 6, rem = nu & 63;
+  if constexpr (!kEarly) {
+    // Two workgroups per compute unit keep the VALU busy to the end: one thread per row adds the
+    // run in range order, so the other workgroup's decode loses no issue slots.
+    if (tid < nc * kChunkRows) {
+      const int cl = tid >> 4, rr = tid & 15;
+      const int ub = cl * ng;   // the chunk's first unit
+      const int lo = range_of(ub, base, rem);
+      const int hi = range_of(ub + ng - 1, base, rem);
+      // lo may have started in the previous chunk: its sum for this chunk is its second one
+      const uint32_t seg = lo * base + min(lo, rem) < ub ? 1u : 0u;
+      float sum = *(lds_f*)(size_t)(PB + ((seg * kLaneGroups + (uint32_t)lo) * kChunkRows + rr) * 4u);
 #pragma unroll 8
-    for (int g = lo + 1; g <= hi; ++g)
-      sum += *(lds_f*)(size_t)(PB + ((uint32_t)g * kChunkRows + (uint32_t)rr) * 4u);
-    const int row = (c0 + cl) * kChunkRows + rr;
-    if (row < d_out) y[row] = f2h(sum);
+      for (int g = lo + 1; g <= hi; ++g)
+        sum += *(lds_f*)(size_t)(PB + ((uint32_t)g * kChunkRows + (uint32_t)rr) * 4u);
+      const int row = (c0 + cl) * kChunkRows + rr;
+      if (row < d_out) y[row] = f2h(sum);
+    }
+  } else {
+    // One workgroup per compute unit: the end is a latency chain, so eight neighbouring lanes take
+    // one row. Lane p adds ranges lo + p, lo + p + 8, ... (N reads, all issued before the first
+    // add), and the eight part sums meet in a fixed tree ((p0 + p1) + (p2 + p3)) + ((p4 + p5) +
+    // (p6 + p7)) by DPP moves, which hands every lane of the eight the same bits.
+    const int p = lane & 7;
+    const int nrows = nc * kChunkRows;
+    auto rows = [&](auto Nc) {
+      constexpr int N = decltype(Nc)::value;   // 8 N ranges per row at most
+      // wave w takes rows 8w .. 8w + 7, then 8w + 128 ...: a wave-uniform trip count, so only
+      // the waves with rows run and each runs whole (the DPP moves read neighbouring lanes)
+      for (int i0 = wave * 8; i0 < nrows; i0 += kThreads / 8) {
+        const int i = i0 + (lane >> 3);
+        const bool valid = i < nrows;
+        const int cl = valid ? i >> 4 : 0, rr = i & 15;
+        const int ub = cl * ng;   // the chunk's first unit
+        const int lo = range_of(ub, base, rem);
+        const int last = valid ? range_of(ub + ng - 1, base, rem) - lo : -1;   // hi - lo
+        // lo may have started in the previous chunk: its sum for this chunk is its second one
+        const bool seg = p == 0 && lo * base + min(lo, rem) < ub;
+        // range lo + p + 8k sits at a0 + 512 k; past hi the reads stay inside both slots
+        // (lo + p + 8k < 128) and are replaced by zeros
+        const uint32_t a0 = PB + ((uint32_t)(lo + p) * kChunkRows + (uint32_t)rr) * 4u;
+        float v[N];
+        v[0] = *(lds_f*)(size_t)(a0 + (seg ? (uint32_t)(kLaneGroups * kChunkRows * 4) : 0u));
+#pragma unroll
+        for (int k = 1; k < N; ++k) v[k] = *(lds_f*)(size_t)(a0 + 512u * (uint32_t)k);
+        float s = 0.0f;
+#pragma unroll
+        for (int k = 0; k < N; ++k) s += p + 8 * k <= last ? v[k] : 0.0f;
+        s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                           0, __builtin_bit_cast(int, s), 0xB1, 0xF, 0xF, false));
+        s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                           0, __builtin_bit_cast(int, s), 0x4E, 0xF, 0xF, false));
+        s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                           0, __builtin_bit_cast(int, s), 0x141, 0xF, 0xF, false));
+        const int row = (c0 + cl) * kChunkRows + rr;
+        if (valid && p == 0 && row < d_out) y[row] = f2h(s);
+      }
+    };
+    // a covering range holds at least one of the chunk's ng units
+    if (ng <= 32)
+      rows(std::integral_constant<int, 4>{});
+    else
+      rows(std::integral_constant<int, 8>{});
   }
 }
 
