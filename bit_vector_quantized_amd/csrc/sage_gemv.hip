@@ -697,6 +697,11 @@ int plan(const sage_matrix_t* mats, const uint16_t* const* xs, uint16_t* const* 
       c += nc;
     }
   }
+  // Workgroups with the most chunks first: they are dispatched first, so their small loads go out
+  // before the other workgroups' packed streams and they start decoding earliest (measured: gate|up
+  // 7.15 -> 6.87-6.96 us with two workgroups per compute unit, q|k|v 4.67 -> 4.61 us with one).
+  std::stable_sort(P->args.wg, P->args.wg + w,
+                   [](uint32_t a, uint32_t b) { return ((a >> 4) & 63u) > ((b >> 4) & 63u); });
   return SAGE_OK;
 }
 
