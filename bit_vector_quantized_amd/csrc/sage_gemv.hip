@@ -429,8 +429,11 @@ __device__ __attribute__((always_inline)) void gemv_wg(const uint8_t* packed, co
 
   // 5. Range sums to LDS (slot 0: the range's first chunk, slot 1: its second). A row's sum is
   // over the ranges that cover its chunk, a contiguous run lo..hi (at most 64, and at most the
-  // chunk's ng units). Both ways below add them in a fixed order, so results are reproducible bit
-  // for bit.
+  // chunk's ng units). The end of a launch is a chain of dependent waits, so eight neighbouring
+  // lanes take one row: lane p adds ranges lo + p, lo + p + 8, ... (N reads, all issued before the
+  // first add), and the eight part sums meet in a fixed tree ((p0 + p1) + (p2 + p3)) + ((p4 + p5)
+  // + (p6 + p7)) by DPP moves, which hands every lane of the eight the same bits: a fixed order,
+  // so results are reproducible bit for bit.
   {
     const uint32_t a = PB + (uint32_t)(rw * kChunkRows + l16) * 4u;
     *(__attribute__((address_space(3))) float*)(size_t)a = split ? acc0 : acc;
@@ -438,30 +441,9 @@ __device__ __attribute__((always_inline)) void gemv_wg(const uint8_t* packed, co
         split ? acc : 0.0f;
   }
   __syncthreads();
-  typedef __attribute__((address_space(3))) const float lds_f;
-  const int base = nu >> 6, rem = nu & 63;
-  if constexpr (!kEarly) {
-    // Two workgroups per compute unit keep the VALU busy to the end: one thread per row adds the
-    // run in range order, so the other workgroup's decode loses no issue slots.
-    if (tid < nc * kChunkRows) {
-      const int cl = tid >> 4, rr = tid & 15;
-      const int ub = cl * ng;   // the chunk's first unit
-      const int lo = range_of(ub, base, rem);
-      const int hi = range_of(ub + ng - 1, base, rem);
-      // lo may have started in the previous chunk: its sum for this chunk is its second one
-      const uint32_t seg = lo * base + min(lo, rem) < ub ? 1u : 0u;
-      float sum = *(lds_f*)(size_t)(PB + ((seg * kLaneGroups + (uint32_t)lo) * kChunkRows + rr) * 4u);
-#pragma unroll 8
-      for (int g = lo + 1; g <= hi; ++g)
-        sum += *(lds_f*)(size_t)(PB + ((uint32_t)g * kChunkRows + (uint32_t)rr) * 4u);
-      const int row = (c0 + cl) * kChunkRows + rr;
-      if (row < d_out) y[row] = f2h(sum);
-    }
-  } else {
-    // One workgroup per compute unit: the end is a latency chain, so eight neighbouring lanes take
-    // one row. Lane p adds ranges lo + p, lo + p + 8, ... (N reads, all issued before the first
-    // add), and the eight part sums meet in a fixed tree ((p0 + p1) + (p2 + p3)) + ((p4 + p5) +
-    // (p6 + p7)) by DPP moves, which hands every lane of the eight the same bits.
+  {
+    typedef __attribute__((address_space(3))) const float lds_f;
+    const int base = nu >> 6, rem = nu & 63;
     const int p = lane & 7;
     const int nrows = nc * kChunkRows;
     auto rows = [&](auto Nc) {
