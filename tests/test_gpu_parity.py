@@ -296,10 +296,12 @@ def test_gemv_range_padding_at_chunk_end():
             check_gemv(f"one chunk {d_out}x{d_in}", c, x, y)
 
 
-@pytest.mark.parametrize("d_in", [2560, 3968])
+@pytest.mark.parametrize("d_in", [2560, 3968, 4224, 8320])
 def test_gemv_range_padding_two_and_three_chunks(d_in):
     """8784 rows = 549 chunks: two or three chunks per workgroup on a 256-CU device, ranges that
-    cross a chunk boundary next to ranges that end exactly at one."""
+    cross a chunk boundary next to ranges that end exactly at one. 4224 and 8320 columns (33 and
+    65 groups) put more than 32 ranges on a chunk, so the final reduction takes eight sums per lane
+    and, for the second and third chunks, reads past range 63 that it must leave out."""
     rng = W.rng_for(141, d_in)
     c = W.draw_codes(rng, 8784, d_in, 64, 4)
     x = W.draw_x(rng, (d_in,))
