@@ -13,7 +13,6 @@ namespace sage {
 namespace {
 
 constexpr int kEncThreads = 256;         // 4 waves; a wave encodes 64 consecutive subvectors of a row
-constexpr uint32_t kEncNowhere = 1u << 30;
 
 __device__ inline __amdgpu_buffer_rsrc_t enc_view(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);

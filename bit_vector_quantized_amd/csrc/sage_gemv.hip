@@ -615,13 +615,15 @@ int plan(const sage_matrix_t* mats, const uint16_t* const* xs, uint16_t* const* 
     total_units += units[i];
     total_chunks += chunks[i];
   }
-  // workgroups: two per compute unit when two fit in its LDS, every compute unit gets two (at
-  // least twice as many chunks as units) and no product gathers its input: eight wavefronts per
-  // SIMD then hide the latency of the table reads better than four. Otherwise one, which requests
-  // its packed units as soon as its small loads have landed (measured: q|k|v's 384 chunks 5.14 ->
-  // 4.90 us with one; gate|up's 1216 chunks 7.38 us with two, 7.76 us with one, and with pi
-  // gathered 8.17 us with two, 8.02 us with one). No more workgroups than there are chunks, and at
-  // least enough that no workgroup has more than kMaxChunks chunks.
+  // workgroups: two per compute unit when two fit in its LDS and every compute unit gets two (at
+  // least twice as many chunks as units; four times as many when a product gathers its input, whose
+  // gather pass then runs over at least two chunks per workgroup): eight wavefronts per SIMD then
+  // hide the latency of the table reads better than four. Otherwise one, which requests its packed
+  // units as soon as its small loads have landed (measured: q|k|v's 384 chunks 5.14 -> 4.90 us with
+  // one; gate|up's 1216 chunks 7.38 us with two, 7.76 us with one; with pi gathered, gate|up
+  // 7.47-7.50 us with two, 7.78-7.81 us with one, but one 9728x2560 matrix (608 chunks) 5.9-6.1 us
+  // with two, 5.3 us with one). No more workgroups than there are chunks, and at least enough that
+  // no workgroup has more than kMaxChunks chunks.
   uint32_t lds_max = 0;
   bool any_gather = false;
   for (int i = 0; i < n; ++i) {
@@ -629,7 +631,7 @@ int plan(const sage_matrix_t* mats, const uint16_t* const* xs, uint16_t* const* 
     any_gather = any_gather || mats[i].pi != nullptr;
   }
   const int per_cu =
-      lds_max <= kMaxLds / 2 && !any_gather && total_chunks >= 2 * (int64_t)cus ? 2 : 1;
+      lds_max <= kMaxLds / 2 && total_chunks >= (any_gather ? 4 : 2) * (int64_t)cus ? 2 : 1;
   int64_t G = std::min<int64_t>((int64_t)cus * per_cu, total_chunks);
   std::vector<int64_t> g(n);
   std::vector<std::pair<double, int>> rema;
