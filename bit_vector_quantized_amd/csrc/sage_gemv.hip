@@ -402,6 +402,11 @@ __device__ __attribute__((always_inline)) void gemv_wg(const uint8_t* packed, co
   }
   __syncthreads();
 
+  // Waves in their decode loop issue ahead of waves still in their set-up (the other workgroup of
+  // the compute unit) and of waves ending theirs: the decode of landed data is the launch's critical
+  // path (measured: layer step 21.07-21.11 -> 20.75-20.89 us, gate|up 6.90-6.91 -> 6.76-6.79 us;
+  // keeping the raised priority through the end gave back most of it).
+  __builtin_amdgcn_s_setprio(2);
   // 4. The packed units (requested here with two workgroups per compute unit), decoded as they
   // land.
   if constexpr (!kEarly) {
@@ -427,6 +432,7 @@ __device__ __attribute__((always_inline)) void gemv_wg(const uint8_t* packed, co
     }
   }
 
+  __builtin_amdgcn_s_setprio(0);
   // 5. Range sums to LDS (slot 0: the range's first chunk, slot 1: its second). A row's sum is
   // over the ranges that cover its chunk, a contiguous run lo..hi (at most 64, and at most the
   // chunk's ng units). The end of a launch is a chain of dependent waits, so eight neighbouring
